@@ -1,0 +1,240 @@
+// LayerNorm (fp32 statistics, one wave per row) and block-diagonal windowed
+// multi-head attention (one workgroup per (window, head)).
+//
+// qwenasr.cpp ARCHITECTURE.md "Windowed audio tower": pre-norm blocks with
+// LayerNorm carrying a bias; bidirectional attention without RoPE, scaled by
+// 1/sqrt(head_dim), confined by a block-diagonal mask to windows of 13 * 8 =
+// 104 tokens; M* ASR page "Graph": one attention segment per window of every
+// request, all in one packed ragged batch (cu_seqlens).  OneSpeech "Front end
+// and graph numerics": scores and softmax stay fp32, the attended output is
+// rounded to bf16.
+#include "qa_device.h"
+#include "qa_kernels.h"
+
+namespace qa {
+
+// ------------------------------------------------------------ LayerNorm
+
+constexpr float kLnEps = 1e-5f;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, int M, int d,
+                                                        const float* __restrict__ g,
+                                                        const float* __restrict__ b, T* __restrict__ out) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M) return;
+    const int d4 = d >> 2;
+    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * d);
+    float4 v[8];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int i = lane + 64 * q;
+        if (i < d4) { v[q] = xr[i]; s += (v[q].x + v[q].y) + (v[q].z + v[q].w); }
+    }
+    const float mean = wave_sum(s) / (float)d;
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int i = lane + 64 * q;
+        if (i < d4) {
+            const float a = v[q].x - mean, bb = v[q].y - mean, c = v[q].z - mean, e = v[q].w - mean;
+            ss += (a * a + bb * bb) + (c * c + e * e);
+        }
+    }
+    const float rstd = rsqrtf(wave_sum(ss) / (float)d + kLnEps);
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+    T* o = out + (size_t)row * d;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int i = lane + 64 * q;
+        if (i < d4) {
+            const float4 gg = g4[i], bb = b4[i];
+            store4(o + 4 * i, (v[q].x - mean) * rstd * gg.x + bb.x, (v[q].y - mean) * rstd * gg.y + bb.y,
+                   (v[q].z - mean) * rstd * gg.z + bb.z, (v[q].w - mean) * rstd * gg.w + bb.w);
+        }
+    }
+}
+
+template <typename T>
+hipError_t layernorm(hipStream_t s, const float* x, int M, int d, const float* g, const float* b, T* out) {
+    if (M <= 0) return hipSuccess;
+    if (d % 4 || d > 2048) return hipErrorInvalidValue;
+    layernorm_kernel<T><<<(M + 3) / 4, 256, 0, s>>>(x, M, d, g, b, out);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ attention
+//
+// Per wave and 16-query tile: S^T = K Q^T on MFMA (keys as rows), so each lane
+// holds one query column and 4 keys per 16-key tile; the softmax over keys
+// reduces in-lane, then across the 4 lane groups with two xor shuffles.  The
+// probabilities then feed O^T = V^T P^T straight from registers: for a
+// 32-key MFMA step the lane's 8 k-slots are its keys {4g..4g+3} of two key
+// tiles, and V^T (kept transposed in LDS) is read at the same keys.
+
+constexpr int kHd = 64;
+
+template <typename T> struct AttnLds;
+template <> struct AttnLds<bf16> {
+    static constexpr int qrow = 144;               // 128 B + 16 pad
+    static constexpr int vrow = 2 * kMaxWindow + 8; // bytes per V^T row (d index)
+};
+template <> struct AttnLds<float> {
+    static constexpr int qrow = 272;               // 256 B + 16 pad
+    static constexpr int vrow = 4 * kMaxWindow + 16;
+};
+
+// P.V over one 32-key step (bf16) or one 16-key tile (fp32), accumulate o[dt].
+__device__ __forceinline__ void pv_step(bf16, const char* vt, int kbase, int fr, int fg, const f32x4* p,
+                                        int t0, f32x4* o) {
+    // slots 0..3: keys kbase + 4g + r (tile t0), slots 4..7: kbase + 16 + 4g + r (tile t0 + 1)
+    bf16x8 pb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { pb[r] = (bf16)p[t0][r]; pb[4 + r] = (bf16)p[t0 + 1][r]; }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const char* row = vt + (dt * 16 + fr) * AttnLds<bf16>::vrow;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 4 * fg));
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 16 + 4 * fg));
+        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[dt], 0, 0, 0);
+    }
+}
+__device__ __forceinline__ void pv_step(float, const char* vt, int kbase, int fr, int fg, const f32x4* p,
+                                        int t0, f32x4* o) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const char* row = vt + (dt * 16 + fr) * AttnLds<float>::vrow;
+        const float4 va = *reinterpret_cast<const float4*>(row + 4 * (kbase + 4 * fg));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, p[t0][0], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, p[t0][1], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, p[t0][2], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, p[t0][3], o[dt], 0, 0, 0);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qkv, const int* __restrict__ cu,
+                                                        int n_heads, int d, T* __restrict__ out) {
+    constexpr int QR = AttnLds<T>::qrow, VR = AttnLds<T>::vrow;
+    constexpr int PER = Elem<T>::per16;
+    constexpr int CPR = kHd / PER;                 // 16-byte chunks per head row
+    __shared__ __align__(16) char qs[kMaxWindow * QR];
+    __shared__ __align__(16) char ks[kMaxWindow * QR];
+    __shared__ __align__(16) char vts[kHd * VR];
+
+    const int win = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
+    const int s0 = cu[win], n = cu[win + 1] - s0;
+    const int tid = threadIdx.x;
+    const size_t ld = 3 * (size_t)d;
+    // Q, K rows (zero beyond n)
+    for (int idx = tid; idx < kMaxWindow * CPR; idx += 256) {
+        const int t = idx / CPR, c = idx % CPR;
+        uint4 qv = zero16(), kv = zero16();
+        if (t < n) {
+            const T* row = qkv + (size_t)(s0 + t) * ld + h * kHd + c * PER;
+            qv = ld16(row);
+            kv = ld16(row + d);
+        }
+        st16(qs + t * QR + c * 16, qv);
+        st16(ks + t * QR + c * 16, kv);
+    }
+    // V^T[dd][t] (zero beyond n)
+    for (int idx = tid; idx < kMaxWindow * kHd; idx += 256) {
+        const int t = idx / kHd, dd = idx % kHd;
+        T v = from_f32<T>(0.f);
+        if (t < n) v = qkv[(size_t)(s0 + t) * ld + 2 * d + h * kHd + dd];
+        *reinterpret_cast<T*>(vts + dd * VR + t * sizeof(T)) = v;
+    }
+    __syncthreads();
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int nt = (n + 15) >> 4;                  // 16-row tiles in this window
+    const float sc = 0.125f * 1.4426950408889634f; // 1/sqrt(64) * log2(e)
+    for (int qt = wave; qt < nt; qt += 4) {
+        f32x4 sacc[8];
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char* qrow = qs + (qt * 16 + fr) * QR + fg * 16;
+#pragma unroll
+        for (int kb = 0; kb < kHd * (int)sizeof(T) / 64; ++kb) {
+            const uint4 qf = ld16(qrow + kb * 64);
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                if (kt < nt) {
+                    const uint4 kf = ld16(ks + (kt * 16 + fr) * QR + fg * 16 + kb * 64);
+                    mfma_kblock(T(), kf, qf, sacc[kt]);
+                }
+            }
+        }
+        // sacc[kt][r] = score(key kt*16 + 4fg + r, query qt*16 + fr)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kt * 16 + 4 * fg + r;
+                const float v = (kt < nt && key < n) ? sacc[kt][r] * sc : -INFINITY;
+                sacc[kt][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float sum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2f(sacc[kt][r] - mx);
+                sacc[kt][r] = p;
+                sum += p;
+            }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        f32x4 o[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (sizeof(T) == 2) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                if (2 * st < nt) pv_step(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+                if (kt < nt) pv_step(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
+        }
+        const int q = qt * 16 + fr;
+        if (q < n) {
+            const float inv = 1.0f / sum;
+            T* orow = out + (size_t)(s0 + q) * d + h * kHd;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                store4(orow + dt * 16 + 4 * fg, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+        }
+    }
+}
+
+template <typename T>
+hipError_t attention(hipStream_t s, const T* qkv, const int* cu_seqlens, int n_windows, int n_heads,
+                     int d, T* out) {
+    if (n_windows <= 0) return hipSuccess;
+    attention_kernel<T><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);
+    return hipGetLastError();
+}
+
+template hipError_t layernorm<float>(hipStream_t, const float*, int, int, const float*, const float*, float*);
+template hipError_t layernorm<bf16>(hipStream_t, const float*, int, int, const float*, const float*, bf16*);
+template hipError_t attention<float>(hipStream_t, const float*, const int*, int, int, int, float*);
+template hipError_t attention<bf16>(hipStream_t, const bf16*, const int*, int, int, int, bf16*);
+
+}  // namespace qa

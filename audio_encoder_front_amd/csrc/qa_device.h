@@ -1,0 +1,67 @@
+// Device-side helpers shared by the gfx950 kernels: element types, 16-byte
+// fragment moves and the MFMA step over one 64-byte K block.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Elem;
+template <> struct Elem<float> { static constexpr int per16 = 4; };   // elements per 16 bytes
+template <> struct Elem<bf16>  { static constexpr int per16 = 8; };
+
+__device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// One MFMA pass over a 64-byte K block held as 16 bytes per lane.
+//   bf16: v_mfma_f32_16x16x32_bf16, lane l holds A[l%16][8g..8g+7] and
+//         B[8g..8g+7][l%16] (g = l/16).
+//   fp32: four v_mfma_f32_16x16x4_f32; float s of the lane's 16 bytes is the
+//         k index 4g+s of the block, identically for A and B, so the product
+//         is the same sum in a permuted order.
+// The result lane l holds D[4g + r][l % 16], r = 0..3.
+__device__ __forceinline__ void mfma_kblock(bf16, const uint4& a, const uint4& b, f32x4& acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_kblock(float, const uint4& a, const uint4& b, f32x4& acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// Exact (erf) GELU.
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+// Store 4 consecutive values (fp32 -> 16 bytes, bf16 -> 8 bytes, RNE).
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// Order-preserving int key of a float, for atomicMax over floats.
+__device__ __forceinline__ int float_key(float f) {
+    int i = __float_as_int(f);
+    return i >= 0 ? i : (i ^ 0x7fffffff);
+}
+__device__ __forceinline__ float key_float(int k) {
+    return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff));
+}
+
+}  // namespace qa

@@ -1,0 +1,83 @@
+// Host-side launch interface of the gfx950 kernels (no device code here).
+// Every function enqueues on `s` and returns hipGetLastError() of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qa {
+
+typedef __bf16 bf16;
+
+// Per-clip bookkeeping: first sample in the packed PCM, sample count, and the
+// global row of the clip's first log-mel frame.
+struct ClipInfo {
+    int64_t sample_off;
+    int32_t len;
+    int32_t frame_row0;
+};
+
+// A front-end tile: up to 64 consecutive frames of one clip.
+struct FrontTile {
+    int32_t clip;
+    int32_t frame0;      // first frame, counted within the clip
+    int32_t nframes;     // 1..64
+    int32_t pad_;
+};
+
+// A 100-frame conv chunk: global log-mel row of its first frame and the
+// number of real frames (the rest of the 100 are zeros).
+struct ChunkInfo {
+    int32_t frame_row0;
+    int32_t m;
+};
+
+constexpr int kMels = 128;
+constexpr int kFrontFrames = 64;     // frames per front-end tile
+constexpr int kBinChunks = 13;       // 13 x 16 = 208 >= 201 DFT bins
+constexpr int kChunk = 100;          // frames per conv chunk
+constexpr int kChunkTok = 13;        // tokens per full chunk
+constexpr int kMaxWindow = 128;      // attention kernel capacity (tokens per window)
+
+// ---- front end
+hipError_t init_flags(hipStream_t s, int* clip_key, int n_clips, int* flag);
+hipError_t frontend(hipStream_t s, const float* pcm, const ClipInfo* clips, const FrontTile* tiles,
+                    int n_tiles, const float* basis, const float* fbB, const int* fb_range,
+                    float* logmel, int* clip_key, int* flag);
+hipError_t normalize(hipStream_t s, float* logmel, const ClipInfo* clips, const FrontTile* tiles,
+                     int n_tiles, const int* clip_key);
+
+// ---- stem
+template <typename T>
+hipError_t conv1(hipStream_t s, const float* logmel, const ChunkInfo* chunks, int n_chunks,
+                 const float* w9c, const float* bias, int C, T* out);
+// conv 3x3 stride 2 pad 1 over NHWC input [n_chunks][Hin][Win][C] as an
+// implicit GEMM; weights [C_out][9*C] with k = (a*3+b)*C + ci.  Output is
+// [n_chunks][Hout][Wout][C] (time_major=false) or [n_chunks][Wout][Hout][C].
+template <typename T>
+hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win, int C,
+                     const T* w, const float* bias, T* out, bool time_major);
+// x[t][:] = A[src[t]][:] . Wout^T + pe[src[t] % 13][:]  (fp32), and optionally
+// tap[t][:] without the PE.
+template <typename T>
+hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K, const T* w, int N,
+                    const float* pe, float* x, float* tap);
+
+// ---- dense GEMMs: out[M][N] = A[M][K] . W[N][K]^T + bias
+template <typename T>
+hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N, const float* bias,
+                     T* out, bool gelu);
+template <typename T>
+hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, int N,
+                           const float* bias, float* x);
+template <typename T>
+hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, int N,
+                         const float* bias, float* out);
+
+// ---- LayerNorm (fp32 in, T out) and windowed attention
+template <typename T>
+hipError_t layernorm(hipStream_t s, const float* x, int M, int d, const float* g, const float* b, T* out);
+template <typename T>
+hipError_t attention(hipStream_t s, const T* qkv, const int* cu_seqlens, int n_windows, int n_heads,
+                     int d, T* out);
+
+}  // namespace qa

@@ -1,0 +1,190 @@
+"""Throughput of the AuT audio-encoder forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b17_20m]
+
+A step is one qa_encode of the whole batch: log-mel front end, conv stem,
+every encoder layer and the output projection, with the PCM and the weights
+already resident in HBM.  Prints one JSON line.  Per-kernel durations come
+from HIP events the library records on its stream around every launch during
+the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "audio-sec encoded/sec (log-mel+AuT encoder), 1 MI355X; MFMA util %"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def plan_counts(lengths, chunk_tok=13, window_chunks=8):
+    """Integer bookkeeping of the batch: chunks (tails padded to 100 frames
+    count as full chunks of stem work), tokens, window sizes, frames."""
+    chunks, tokens, frames, windows = 0, 0, 0, []
+    for n in lengths:
+        nf = n // 160
+        frames += nf
+        full, tail = divmod(nf, 100)
+        chunks += full + (1 if tail else 0)
+        t = full * chunk_tok + ((tail + 7) // 8 if tail else 0)
+        tokens += t
+        w = chunk_tok * window_chunks
+        windows += [min(w, t - s) for s in range(0, t, w)]
+    return chunks, tokens, frames, windows
+
+
+def kernel_work(d, lengths):
+    """Algorithmic work per launch of each labelled kernel: (flops, bytes,
+    peak label).  Flops count dense MACs as 2; bytes count compulsory HBM
+    traffic (operands read once, results written once)."""
+    C, D, F, O, H = d.conv_channels, d.d_model, d.ffn_dim, d.output_dim, d.n_heads
+    ch, T, fr, wins = plan_counts(lengths, window_chunks=d.window_chunks)
+    e = 2 if d.dtype == "bf16" else 4
+    work = {
+        "frontend": (fr * (2 * 400 * 400 + 2 * 201 * 128), sum(lengths) * 4 + fr * 128 * 4, "fp32"),
+        "conv2": (2 * ch * 800 * C * 9 * C, ch * 64 * 50 * C * e + ch * 800 * C * e + 9 * C * C * e, "bf16"),
+        "conv3": (2 * ch * 208 * C * 9 * C, ch * 800 * C * e + ch * 208 * C * e + 9 * C * C * e, "bf16"),
+        "conv_out": (2 * T * 16 * C * D, T * 16 * C * e + 16 * C * D * e + T * D * 4, "bf16"),
+        "qkv": (2 * T * D * 3 * D, T * D * e + 3 * D * D * e + T * 3 * D * e, "bf16"),
+        "attention": (sum(4 * n * n * 64 * H for n in wins), T * 3 * D * e + T * D * e, "bf16"),
+        "o_proj": (2 * T * D * D, T * D * e + D * D * e + 2 * T * D * 4, "bf16"),
+        "fc1": (2 * T * D * F, T * D * e + F * D * e + T * F * e, "bf16"),
+        "fc2": (2 * T * F * D, T * F * e + F * D * e + 2 * T * D * 4, "bf16"),
+        "proj1": (2 * T * D * D, T * D * e + D * D * e + T * D * e, "bf16"),
+        "proj2": (2 * T * D * O, T * D * e + O * D * e + T * O * 4, "bf16"),
+        "ln": (0, T * D * 4 + T * D * e, "hbm"),
+        "conv1": (2 * ch * 64 * 50 * C * 9, fr * 128 * 4 + ch * 64 * 50 * C * e, "fp32"),
+        "normalize": (0, 2 * fr * 128 * 4, "hbm"),
+    }
+    return work, (ch, T, fr, wins)
+
+
+def cpu_baseline(wl, seconds: float):
+    """The fp64 oracle on the first `seconds` of the workload's first clip."""
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
+    except Exception:  # pragma: no cover
+        threads, blas = os.cpu_count(), "?"
+    clip = synth.make_audio(wl)[0][: int(seconds * 16000)]
+    w = synth.make_weights(wl.dims, wl.weight_seed)
+    t0 = time.perf_counter()
+    out = O.encode([clip], w, wl.dims.n_layers, wl.dims.n_heads, window_chunks=wl.dims.window_chunks)
+    dt = time.perf_counter() - t0
+    return {"value": len(clip) / 16000.0 / dt, "unit": "audio-s/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {seconds:g} s of the clip as one clip ({out.shape[0]} tokens), fp64 NumPy "
+                      f"({blas}), {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="b17_20m")
+    ap.add_argument("--cpu-sample-s", type=float, default=32.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the encoder runs on a single MI355X and this build has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import audio_encoder_front_amd as qa
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    clips = synth.make_audio(wl)
+    lengths = [len(c) for c in clips]
+    weights = synth.make_weights(wl.dims, wl.weight_seed)
+    dev = torch.device("cuda:0")
+    pcm = torch.from_numpy(np.concatenate(clips)).to(dev)
+    enc = qa.qa_encoder_create(weights, wl.dims)
+    del weights
+    stream = torch.cuda.current_stream(dev)
+    qa.qa_encoder_set_stream(enc, stream)
+    total_tok = sum(qa.qa_encode_num_tokens(n) for n in lengths)
+    out = torch.empty((total_tok, wl.dims.output_dim), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        qa.qa_encode(enc, pcm, lengths, out)
+    torch.cuda.synchronize()
+    qa.qa_encoder_set_profiling(enc, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        qa.qa_encode(enc, pcm, lengths, out)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    times = qa.qa_encoder_kernel_times(enc)
+    qa.qa_encoder_set_profiling(enc, False)
+
+    audio_s = sum(lengths) / 16000.0
+    ms_step = dt / args.steps * 1e3
+    work, (n_chunks, T, n_frames, wins) = kernel_work(wl.dims, lengths)
+    total_flops = sum(work[l][0] * cnt for l, (_, cnt) in times.items() if l in work) / args.steps
+    kernels = {}
+    for label, (ms, cnt) in sorted(times.items()):
+        avg = ms / max(cnt, 1)
+        ent = {"avg_ms": round(avg, 5), "launches": int(cnt), "total_ms_per_step": round(ms / args.steps, 4)}
+        if label in work:
+            f, b, kind = work[label]
+            if f:
+                ent["tflops"] = round(f / (avg * 1e-3) / 1e12, 2)
+            if b:
+                ent["gbs"] = round(b / (avg * 1e-3) / 1e9, 1)
+        kernels[label] = ent
+    # dominant kernel: largest total time among the labelled compute kernels
+    dom = max((l for l in kernels if l in work), key=lambda l: kernels[l]["total_ms_per_step"])
+    f, b, kind = work[dom]
+    avg_s = kernels[dom]["avg_ms"] * 1e-3
+    if kind == "hbm":
+        roof = {"bound": "hbm", "achieved": b / avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        peak = PEAK_BF16_TFLOPS if kind == "bf16" else PEAK_FP32_MFMA_TFLOPS
+        roof = {"bound": "mfma", "achieved": f / avg_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["per_launch"] = {"flops": f, "bytes": b}
+    res = {
+        "metric": METRIC,
+        "value": round(audio_s * args.steps / dt, 2),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dims.dtype,
+        "data": "synthetic (seeded speech-like PCM, N(0,0.02) bf16 weights)",
+        "config": {"workload": f"{wl.name}: {wl.description}", "clips": len(lengths), "audio_s": audio_s,
+                   "tokens": T, "windows": len(wins), "chunks": n_chunks, "frames": n_frames},
+        "tokens_per_s": round(T * args.steps / dt, 1),
+        "mfma_util_pct": round(100.0 * total_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 2),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_s)
+    enc.free()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * qa_encoder.h -- C ABI of the MI355X (gfx950) AuT audio-encoder forward.
+ *
+ * Plain C99, no PyTorch or HIP types.  The library computes, for a packed
+ * batch of 16 kHz mono clips, the Qwen3-ASR audio tower:
+ *
+ *   PCM -> 128-bin Whisper log-mel (n_fft 400, hop 160, periodic Hann,
+ *          centered reflection, Slaney mel 0-8 kHz, floor 1e-10, log10,
+ *          peak-minus-8 clip, (x+4)/4; the last STFT frame is dropped)
+ *       -> per 100-frame chunk: three conv2d (k3, s2, p1) + bias + erf-GELU,
+ *          flatten channel-outer / frequency-inner, conv_out Linear (no bias),
+ *          plus a sinusoidal position table that restarts at every chunk
+ *       -> n_layers pre-LN transformer blocks whose bidirectional attention is
+ *          confined to windows of 13 * window_chunks tokens of each clip
+ *       -> post LayerNorm, proj1 (d -> d), GELU, proj2 (d -> output_dim).
+ *
+ * Sources (pages on Qwen3-ASR):
+ *   OneSpeech Qwen3 docs, "Front end and graph numerics" (features, chunks,
+ *     PE reset, bf16 operator-boundary policy) and "Low-level recognition"
+ *     (input rules: empty allowed, nonempty > 200 samples, nonfinite rejected);
+ *   qwenasr.cpp ARCHITECTURE.md, "GGUF layout" (dims and tensor inventory),
+ *     "Mel frontend", "Conv2d subsampling stem", "Windowed audio tower",
+ *     "Public API" (status codes, thread-local last error, ABI version);
+ *   M* ASR page, Qwen3-ASR "Graph" (one packed forward per batch, one attention
+ *     segment per window of every request; requests up to 20 minutes).
+ */
+#ifndef QA_ENCODER_H
+#define QA_ENCODER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QA_ABI_VERSION 1
+
+/* Status codes (qwenasr.cpp "Public API" numbering). */
+#define QA_STATUS_OK              0
+#define QA_STATUS_INVALID_PARAMS (-1)
+#define QA_STATUS_LOAD_FAILED    (-2)
+#define QA_STATUS_ENCODE_FAILED  (-3)
+#define QA_STATUS_OOM            (-4)
+
+/* Element type of the weights handed to qa_encoder_create, and the operand
+ * precision of every contraction.  QA_DTYPE_BF16: bf16 operands rounded to
+ * nearest-even at operator boundaries, fp32 accumulation, fp32 residual
+ * stream, LayerNorm statistics and softmax (OneSpeech "Front end and graph
+ * numerics").  The DFT and mel contractions are fp32 in both modes. */
+#define QA_DTYPE_F32  0
+#define QA_DTYPE_BF16 1
+
+/* Tap ids for qa_encoder_tap (stage outputs of the last qa_encode). */
+#define QA_TAP_LOG_MEL 0   /* normalised log-mel, fp32 [total_frames x 128], frame-major, clips in order */
+#define QA_TAP_STEM    1   /* conv_out output before PE, fp32 [total_tokens x d_model] */
+#define QA_TAP_LAYER0  2   /* residual stream after encoder layer 0, fp32 [total_tokens x d_model] */
+
+/* Encoder dimensions; the field names follow the audio.* metadata keys of the
+ * qwenasr.cpp "GGUF layout" section. */
+typedef struct qa_dims {
+    int abi_version;      /* must equal QA_ABI_VERSION */
+    int n_mels;           /* num_mel_bins: must be 128 */
+    int conv_channels;    /* downsample_hidden_size (480); multiple of 32, <= 1024 */
+    int d_model;          /* multiple of 64, <= 2048 */
+    int n_layers;         /* encoder_layers, >= 0 */
+    int n_heads;          /* encoder_attention_heads; n_heads * head_dim == d_model */
+    int head_dim;         /* must be 64 */
+    int ffn_dim;          /* encoder_ffn_dim, multiple of 64 */
+    int output_dim;       /* output_dim, multiple of 64 */
+    int chunk_frames;     /* n_window * 2: must be 100 */
+    int window_chunks;    /* n_window_infer / chunk_frames: 1..8 (8 -> 104-token windows) */
+    int dtype;            /* QA_DTYPE_F32 or QA_DTYPE_BF16 */
+} qa_dims;
+
+/* Weights: HOST pointers in PyTorch layouts, element type = dims.dtype
+ * (QA_DTYPE_BF16: uint16 bfloat16 bit patterns; QA_DTYPE_F32: float).
+ *   conv{1,2,3}_w  [C, C_in, 3 (mel), 3 (time)], C_in = 1 for conv1;  conv*_b [C]
+ *   conv_out_w     [d_model, C * 16], input index c * 16 + f (no bias)
+ *   per layer (arrays of n_layers pointers):
+ *     ln1_w/b, ln2_w/b [d]; q/k/v/o_w [d, d]; q/k/v/o_b [d];
+ *     fc1_w [ffn, d], fc1_b [ffn]; fc2_w [d, ffn], fc2_b [d]
+ *   post_ln_w/b [d]; proj1_w [d, d], proj1_b [d]; proj2_w [out, d], proj2_b [out]
+ * The library copies (and repacks) everything; the caller may free its
+ * buffers as soon as qa_encoder_create returns. */
+typedef struct qa_weights {
+    const void *conv1_w, *conv1_b, *conv2_w, *conv2_b, *conv3_w, *conv3_b, *conv_out_w;
+    const void *const *ln1_w, *const *ln1_b;
+    const void *const *q_w, *const *q_b, *const *k_w, *const *k_b, *const *v_w, *const *v_b;
+    const void *const *o_w, *const *o_b;
+    const void *const *ln2_w, *const *ln2_b;
+    const void *const *fc1_w, *const *fc1_b, *const *fc2_w, *const *fc2_b;
+    const void *post_ln_w, *post_ln_b, *proj1_w, *proj1_b, *proj2_w, *proj2_b;
+} qa_weights;
+
+typedef struct qa_encoder qa_encoder;   /* opaque */
+
+/* ABI version the library was built with. */
+int qa_abi_version(void);
+
+/* Thread-local message describing the most recent failure on this thread
+ * (never NULL; "" if none). */
+const char *qa_last_error(void);
+
+/* Number of encoder tokens (output rows) of one clip of n_samples samples,
+ * with 100-frame chunks: F = n_samples / 160 frames, 13 tokens per full chunk
+ * and ceil(m / 8) for a tail of m frames.  0 for an empty clip; -1 (and
+ * qa_last_error set) if 1 <= n_samples <= 200, n_samples < 0 or n_samples >
+ * 19,200,000 (20 minutes).  Pure host arithmetic. */
+int64_t qa_encode_num_tokens(int64_t n_samples);
+
+/* Validate dims and weights, copy and repack the weights into device memory
+ * of the current HIP device.  Returns NULL on failure (qa_last_error says
+ * why): invalid dims or NULL weight pointers -> INVALID_PARAMS semantics,
+ * device allocation or copy failure -> LOAD_FAILED semantics. */
+qa_encoder *qa_encoder_create(const qa_weights *w, const qa_dims *d);
+
+/* Enqueue all later work of this handle on `hip_stream` (a hipStream_t;
+ * NULL = the null stream).  Returns QA_STATUS_OK or INVALID_PARAMS. */
+int qa_encoder_set_stream(qa_encoder *e, void *hip_stream);
+
+/* Encode a packed batch.
+ *   pcm      DEVICE pointer, float32, all clips concatenated in `lengths`
+ *            order (sum(lengths) samples, 16 kHz mono).  Caller-owned.
+ *   lengths  HOST array of n_clips int64 sample counts.  0 = empty clip (no
+ *            tokens); otherwise 201 .. 19,200,000.
+ *   n_clips  >= 0.
+ *   out      DEVICE pointer, float32 [sum_i qa_encode_num_tokens(lengths[i])
+ *            x output_dim], rows clip-major, then chunk, then token-in-chunk.
+ *            Caller-owned; may be NULL when the total is 0.
+ * All argument checks happen before any device work.  The work is enqueued
+ * on the handle's stream; the call then synchronises that stream to read a
+ * device-side validation flag.  Returns QA_STATUS_OK; INVALID_PARAMS for bad
+ * arguments, a nonfinite sample or a mel energy beyond float32 range (then
+ * `out` is unspecified); OOM if the workspace cannot grow; ENCODE_FAILED on a
+ * launch/runtime error.  Calls on one handle must not overlap. */
+int qa_encode(qa_encoder *e, const float *pcm, const int64_t *lengths, int n_clips, float *out);
+
+/* Keep stage outputs of later qa_encode calls for qa_encoder_tap (costs one
+ * extra conv_out GEMM and a copy per call).  enable: 0 or 1. */
+int qa_encoder_enable_taps(qa_encoder *e, int enable);
+
+/* Copy tap `tap` (QA_TAP_*) of the last qa_encode into the DEVICE buffer dst
+ * (capacity in float elements), synchronously on the handle's stream.
+ * Returns the element count copied, or -1 (taps disabled, unknown tap, or
+ * capacity too small; qa_last_error set). */
+int64_t qa_encoder_tap(qa_encoder *e, int tap, float *dst, int64_t capacity);
+
+/* Per-kernel timing with HIP events recorded on the handle's stream around
+ * every launch (0 disables; the default).  qa_encoder_kernel_times fills up
+ * to `cap` entries of: a static NUL-terminated label, the summed
+ * milliseconds and the launch count accumulated since profiling was last
+ * enabled, and returns the number of labels (which may exceed cap). */
+int qa_encoder_set_profiling(qa_encoder *e, int enable);
+int qa_encoder_kernel_times(qa_encoder *e, const char **labels, double *total_ms,
+                            int64_t *launches, int cap);
+
+/* Release device memory and the handle.  NULL is a no-op. */
+void qa_encoder_free(qa_encoder *e);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QA_ENCODER_H */

@@ -112,13 +112,24 @@ def mel_filterbank(n_mels: int = N_MELS, n_fft: int = N_FFT, sr: int = SAMPLE_RA
     return fb
 
 
+F32_MAX = float(np.finfo(np.float32).max)
+
+
 def log_mel_raw(x: np.ndarray) -> np.ndarray:
     """log10(max(mel energy, 1e-10)) for the kept frames, [n_mels, F] with
     F = floor(len/160) ([qwenasr] "Mel frontend": clamp then log; the trailing
-    STFT frame is dropped; [OneSpeech] "power floor 1e-10")."""
+    STFT frame is dropped; [OneSpeech] "power floor 1e-10").
+
+    Raises InvalidInput for a nonfinite sample or a power / mel value beyond
+    float32 range ([OneSpeech] "Low-level recognition": such inputs are
+    rejected)."""
+    if not np.all(np.isfinite(x)):
+        raise InvalidInput("nonfinite sample")
     fr = stft_frames(x)
     p = power_spectrum(fr)                 # [F+1, 201]
     e = p @ mel_filterbank().T             # [F+1, 128]
+    if p.max(initial=0.0) > F32_MAX or e.max(initial=0.0) > F32_MAX:
+        raise InvalidInput("power beyond float32 range")
     lg = np.log10(np.maximum(e, 1e-10))
     return lg[:-1].T                       # drop the last frame, mel-major
 

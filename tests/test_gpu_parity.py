@@ -1,0 +1,174 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle on
+the same seeded inputs.  Tolerances: normalised log-mel max-abs 1e-4 (fp32
+encoder) / 2e-3 (bf16), per-window relative L2 of the output 1e-4 / 1e-2; the
+pre-PE stem output and the layer-0 residual are checked per window too."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from parity_util import compare, make_encoder, run_gpu, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl, clips, w = workload_inputs("tiny")
+    enc = make_encoder(wl.dims, w)
+    yield wl, clips, w, enc
+    enc.free()
+
+
+def test_tiny_workload_full_parity(tiny):
+    wl, clips, w, enc = tiny
+    _print("case: tiny workload, 1 clip x 32000 samples, fp32")
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(wl.dims, w, clips, out, taps)
+    _print("tiny", rep)
+
+
+def test_tiny_encoder_ragged_batch(tiny):
+    # several front-end tiles, two GEMM row tiles, tail chunks of 1, 25, 75
+    # and 99 frames, an empty clip, a 1-frame clip and a ragged 2-window clip
+    wl, _, w, enc = tiny
+    lens = [201, 16160, 0, 15999, 100000, 140000, 16000 * 3 + 160 * 99 + 37]
+    clips = [synth.speech_like_clip(n, [77, i]) for i, n in enumerate(lens)]
+    _print("case: tiny encoder ragged batch", lens)
+    out, taps = run_gpu(enc, clips, taps=True)
+    assert out.shape[0] == sum(O.clip_num_tokens(n) for n in lens)
+    rep = compare(wl.dims, w, clips, out, taps)
+    _print("ragged", rep)
+
+
+def test_tiny_encoder_silence_and_tone_edges(tiny):
+    wl, _, w, enc = tiny
+    t = np.arange(48000) / 16000.0
+    clips = [np.zeros(20000, np.float32),                                   # digital silence -> -1.5
+             (0.3 * np.sin(2 * np.pi * 440 * t)).astype(np.float32),         # noise-free tone
+             synth.speech_like_clip(64000, [78, 0])]
+    clips[2][10000:30000] = 0.0                                             # clamp active
+    _print("case: silence / tone / gap")
+    out, taps = run_gpu(enc, clips, taps=True)
+    nf0 = 20000 // 160
+    assert np.all(taps["log_mel"][:nf0] == -1.5)
+    compare(wl.dims, w, clips, out, taps)
+
+
+def test_rejects_nonfinite_and_short_clips(tiny):
+    import torch
+    import audio_encoder_front_amd as qa
+    wl, _, w, enc = tiny
+    x = synth.speech_like_clip(8000, [79, 0])
+    x[1234] = np.nan
+    pcm = torch.from_numpy(x).cuda()
+    out = torch.empty((qa.qa_encode_num_tokens(8000), 256), device="cuda")
+    with pytest.raises(qa.QAError) as ei:
+        qa.qa_encode(enc, pcm, [8000], out)
+    assert ei.value.status == qa._binding.QA_STATUS_INVALID_PARAMS
+    x[1234] = 1e25                      # power beyond float32 range
+    pcm = torch.from_numpy(x).cuda()
+    with pytest.raises(qa.QAError):
+        qa.qa_encode(enc, pcm, [8000], out)
+    with pytest.raises(qa.QAError):
+        qa.qa_encode(enc, pcm[:200], [200], out)
+    # the handle still works after rejected calls
+    x = synth.speech_like_clip(8000, [79, 1])
+    res, _ = run_gpu(enc, [x])
+    compare(wl.dims, w, [x], res, None)
+
+
+def test_repeated_calls_shrink_and_grow_and_are_deterministic(tiny):
+    wl, _, w, enc = tiny
+    big = [synth.speech_like_clip(n, [80, i]) for i, n in enumerate((150000, 33333))]
+    small = [synth.speech_like_clip(9000, [81, 0])]
+    a, _ = run_gpu(enc, big)
+    b, _ = run_gpu(enc, small)
+    c, _ = run_gpu(enc, big)
+    assert np.array_equal(a, c)
+    compare(wl.dims, w, small, b, None)
+
+
+def test_empty_batch(tiny):
+    wl, _, w, enc = tiny
+    out, _ = run_gpu(enc, [np.zeros(0, np.float32), np.zeros(0, np.float32)])
+    assert out.shape == (0, 256)
+
+
+@pytest.fixture(scope="module")
+def b06():
+    wl, clips, w = workload_inputs("b06_1")
+    enc = make_encoder(wl.dims, w)
+    yield wl, clips, w, enc
+    enc.free()
+
+
+def test_b06_single_30s_full_parity(b06):
+    wl, clips, w, enc = b06
+    _print("case: 0.6B bf16, one 30 s clip")
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(wl.dims, w, clips, out, taps)
+    _print("b06_1", rep)
+
+
+def test_b06_packed_32_clips(b06):
+    wl, _, w, enc = b06
+    wl32 = synth.WORKLOADS["b06_32"]
+    clips = synth.make_audio(wl32)
+    _print("case: 0.6B bf16, 32 clips U(1,30) s")
+    out, taps = run_gpu(enc, clips, taps=True)
+    lens = [len(c) for c in clips]
+    order = np.argsort(lens)
+    picked = {int(order[0]), int(order[-1]), 7}
+    # every window of three clips (shortest, longest, one fixed), the last
+    # (ragged) window of all others; the log-mel of every clip
+    rep = compare(wl.dims, w, clips, out, taps,
+                  windows_per_clip=lambda ci, nw: range(nw) if ci in picked else [nw - 1])
+    _print("b06_32", rep)
+
+
+def test_b06_window_boundaries_and_tails(b06):
+    wl, _, w, enc = b06
+    # 104 tokens exactly (8 chunks), 105 tokens (8 chunks + 1-frame tail),
+    # 9 chunks (117 tokens, a ragged 13-token second window), 1 frame
+    lens = [800 * 160, 801 * 160 + 5, 900 * 160, 201]
+    clips = [synth.speech_like_clip(n, [82, i]) for i, n in enumerate(lens)]
+    out, taps = run_gpu(enc, clips, taps=True)
+    assert out.shape[0] == 104 + 105 + 117 + 1
+    compare(wl.dims, w, clips, out, taps)
+
+
+@pytest.fixture(scope="module")
+def b17():
+    wl = synth.WORKLOADS["b17_20m"]
+    w = synth.make_weights(wl.dims, wl.weight_seed)
+    enc = make_encoder(wl.dims, w)
+    yield wl, w, enc
+    enc.free()
+
+
+def test_b17_twenty_minutes_sampled_windows(b17):
+    wl, w, enc = b17
+    clips = synth.make_audio(wl)
+    _print("case: 1.7B bf16, one 20-minute clip (sampled windows)")
+    out, taps = run_gpu(enc, clips, taps=True)
+    assert out.shape == (15600, 2048)
+    assert np.all(np.isfinite(out))
+    rep = compare(wl.dims, w, clips, out, taps, windows_per_clip=lambda ci, nw: [0, 1, 73, nw - 2, nw - 1])
+    _print("b17_20m", rep)
+
+
+def test_b17_packed_16_clips_sampled_windows(b17):
+    wl, w, enc = b17
+    clips = synth.make_audio(synth.WORKLOADS["b17_16"])
+    _print("case: 1.7B bf16, 16 clips logU(10,300) s (sampled windows)")
+    out, taps = run_gpu(enc, clips, taps=True)
+    assert out.shape == (21162, 2048)
+    shortest = int(np.argmin([len(c) for c in clips]))
+    rep = compare(wl.dims, w, clips, out, taps,
+                  windows_per_clip=lambda ci, nw: range(nw) if ci == shortest else [0, nw - 1])
+    _print("b17_16", rep)

@@ -153,3 +153,15 @@ def test_input_contract():
     O.validate_clip(0)
     O.validate_clip(201)
     O.validate_clip(GOLD["twenty_minutes"]["samples"])
+
+
+def test_rejects_nonfinite_and_float32_overflow():
+    x = synth.speech_like_clip(8000, [79, 0]).astype(np.float64)
+    x[1234] = np.nan
+    with pytest.raises(O.InvalidInput):
+        O.log_mel(x)
+    x[1234] = 1e25                      # |X|^2 ~ 1e50 > float32 max
+    with pytest.raises(O.InvalidInput):
+        O.log_mel(x)
+    x[1234] = 1e3                       # large but representable
+    assert np.all(np.isfinite(O.log_mel(x)))
