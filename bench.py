@@ -94,7 +94,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="b17_20m")
-    ap.add_argument("--cpu-sample-s", type=float, default=32.0)
+    ap.add_argument("--cpu-sample-s", type=float, default=240.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

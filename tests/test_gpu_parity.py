@@ -55,7 +55,8 @@ def test_tiny_encoder_silence_and_tone_edges(tiny):
     _print("case: silence / tone / gap")
     out, taps = run_gpu(enc, clips, taps=True)
     nf0 = 20000 // 160
-    assert np.all(taps["log_mel"][:nf0] == -1.5)
+    # log10 of the 1e-10 floor in fp32 is -10 to within an ulp: -1.5 +- 1e-6
+    assert np.abs(taps["log_mel"][:nf0] + 1.5).max() <= 1e-6
     compare(wl.dims, w, clips, out, taps)
 
 
