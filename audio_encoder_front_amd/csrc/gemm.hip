@@ -12,31 +12,61 @@
 //
 // Layout: both operands are K-contiguous rows (activations [M][K], PyTorch
 // Linear weights [N][K]).  A workgroup of WM x WN waves computes a BM x BN
-// tile; LDS holds two stages of 128-byte K slices per row (64 bf16 or 32
-// fp32 elements) with a 16-byte pad per row, so the 16-byte fragment reads of
-// 8 consecutive rows hit disjoint banks.  The MFMA is issued transposed
-// (weights as the A operand): lane l then holds 4 consecutive output columns
-// of one output row, which makes bias loads and stores 8/16-byte vectors.
-// Global loads of stage k+1 are in flight while stage k is multiplied.
+// tile in stages of 128 bytes of K (64 bf16 or 32 fp32 elements).
+//
+// Staging: every 16-byte chunk moves global -> LDS with one direct-to-LDS
+// load (global_load_lds_dwordx4), no register round trip.  Such a load
+// writes 64 lanes x 16 B contiguously, i.e. 8 LDS rows of 128 B; lane l
+// therefore fetches K-chunk (l%8) ^ (row%8) of its row, an XOR swizzle that
+// makes the 16-byte fragment reads of 8 consecutive rows hit 8 different
+// 16-byte bank groups.  Chunks outside the matrix (ragged M/N/K, conv
+// padding) are fetched from a 16-byte zero block.  Two LDS stages: loads of
+// stage k+1 run while stage k is multiplied.
+//
+// The MFMA is issued transposed (weights as the A operand): lane l then holds
+// 4 consecutive output columns of one output row, so bias loads and stores
+// are 8/16-byte vectors.  Workgroups are remapped so that each of the 8 XCDs
+// works through a contiguous, M-grouped range of tiles (L2 reuse of both
+// operand tiles).
 #include "qa_device.h"
 #include "qa_kernels.h"
 
 namespace qa {
 
-constexpr int kRowBytes = 144;   // 128 data bytes + 16 pad per LDS row
+__device__ __align__(16) uint4 g_zero16[2];
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_wave_base, 16, 0, 0);
+}
 
 // ------------------------------------------------------------ A loaders
-// prep(m) is evaluated once per thread and row; load(ctx, k0) returns the 16
-// bytes of elements [k0, k0 + per16) of row m, or zeros outside the matrix.
+// A loader keeps a compact per-lane state for the AI rows the lane fetches
+// (rows r, r + 8, ..., r + 8 (AI-1) of the tile); kprep(k0) is evaluated once
+// per stage; addr(lane, q, kx) gives the source of elements [k0, k0 + per16)
+// of row q, or g_zero16 outside the matrix.
 
 template <typename T>
 struct DenseA {
     const T* a;
     int M, K, lda;
-    struct Ctx { const T* p; };
-    __device__ Ctx prep(int m) const { return Ctx{m < M ? a + (size_t)m * lda : nullptr}; }
-    __device__ uint4 load(const Ctx& c, int k0) const {
-        return (c.p && k0 < K) ? ld16(c.p + k0) : zero16();
+    template <int AI>
+    struct Lane { const char* base; unsigned valid; };
+    struct KCtx { int off; bool ok; };
+    template <int AI>
+    __device__ Lane<AI> init(int m) const {
+        Lane<AI> l{reinterpret_cast<const char*>(a + (size_t)m * lda), 0u};
+#pragma unroll
+        for (int q = 0; q < AI; ++q) l.valid |= (m + 8 * q < M ? 1u : 0u) << q;
+        return l;
+    }
+    __device__ KCtx kprep(int k0) const { return KCtx{k0 * (int)sizeof(T), k0 < K}; }
+    template <int AI>
+    __device__ const void* addr(const Lane<AI>& l, int q, const KCtx& k) const {
+        return (((l.valid >> q) & 1u) && k.ok)
+                   ? (const void*)(l.base + (size_t)q * 8 * lda * sizeof(T) + k.off)
+                   : (const void*)g_zero16;
     }
 };
 
@@ -45,10 +75,22 @@ struct GatherA {   // row m of the GEMM is row src[m] of a
     const T* a;
     const int* src;
     int M, K;
-    struct Ctx { const T* p; };
-    __device__ Ctx prep(int m) const { return Ctx{m < M ? a + (size_t)src[m] * K : nullptr}; }
-    __device__ uint4 load(const Ctx& c, int k0) const {
-        return (c.p && k0 < K) ? ld16(c.p + k0) : zero16();
+    template <int AI>
+    struct Lane { int row[AI]; };
+    struct KCtx { int off; bool ok; };
+    template <int AI>
+    __device__ Lane<AI> init(int m) const {
+        Lane<AI> l;
+#pragma unroll
+        for (int q = 0; q < AI; ++q) l.row[q] = m + 8 * q < M ? src[m + 8 * q] : -1;
+        return l;
+    }
+    __device__ KCtx kprep(int k0) const { return KCtx{k0 * (int)sizeof(T), k0 < K}; }
+    template <int AI>
+    __device__ const void* addr(const Lane<AI>& l, int q, const KCtx& k) const {
+        return (l.row[q] >= 0 && k.ok)
+                   ? (const void*)(reinterpret_cast<const char*>(a + (size_t)l.row[q] * K) + k.off)
+                   : (const void*)g_zero16;
     }
 };
 
@@ -57,23 +99,38 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv over NHWC inp
     const T* in;
     int M, Hin, Win, C, Hout, Wout;
     bool time_major;                  // output row order (chunk, j, i) instead of (chunk, i, j)
-    struct Ctx { const T* base; int r0, c0; };
-    __device__ Ctx prep(int m) const {
-        if (m >= M) return Ctx{nullptr, 0, 0};
+    template <int AI>
+    struct Lane { int chunk[AI]; int rc[AI]; };   // rc = (2i-1) << 16 | (2j-1) & 0xffff
+    struct KCtx { int a, b, off; bool ok; };
+    template <int AI>
+    __device__ Lane<AI> init(int m0) const {
+        Lane<AI> l;
         const int per = Hout * Wout;
-        const int chunk = m / per, rem = m - chunk * per;
-        int i, j;
-        if (time_major) { j = rem / Hout; i = rem - j * Hout; }
-        else            { i = rem / Wout; j = rem - i * Wout; }
-        return Ctx{in + (size_t)chunk * Hin * Win * C, 2 * i - 1, 2 * j - 1};
+#pragma unroll
+        for (int q = 0; q < AI; ++q) {
+            const int m = m0 + 8 * q;
+            const int chunk = m / per, rem = m - chunk * per;
+            int i, j;
+            if (time_major) { j = rem / Hout; i = rem - j * Hout; }
+            else            { i = rem / Wout; j = rem - i * Wout; }
+            l.chunk[q] = m < M ? chunk : -1;
+            l.rc[q] = ((2 * i - 1) << 16) | ((2 * j - 1) & 0xffff);
+        }
+        return l;
     }
-    __device__ uint4 load(const Ctx& c, int k0) const {
-        if (!c.base || k0 >= 9 * C) return zero16();
+    __device__ KCtx kprep(int k0) const {
         const int tap = k0 / C, ci = k0 - tap * C;
-        const int a = tap / 3, b = tap - a * 3;
-        const int r = c.r0 + a, col = c.c0 + b;
-        if ((unsigned)r >= (unsigned)Hin || (unsigned)col >= (unsigned)Win) return zero16();
-        return ld16(c.base + ((size_t)r * Win + col) * C + ci);
+        const int a = tap / 3;
+        return KCtx{a, tap - 3 * a, ci * (int)sizeof(T), tap < 9};
+    }
+    template <int AI>
+    __device__ const void* addr(const Lane<AI>& l, int q, const KCtx& k) const {
+        const int r = (l.rc[q] >> 16) + k.a;
+        const int col = (int)(short)(l.rc[q] & 0xffff) + k.b;
+        if (l.chunk[q] < 0 || !k.ok || (unsigned)r >= (unsigned)Hin || (unsigned)col >= (unsigned)Win)
+            return g_zero16;
+        return reinterpret_cast<const char*>(in + ((size_t)l.chunk[q] * Hin * Win + (size_t)r * Win + col) * C) +
+               k.off;
     }
 };
 
@@ -137,50 +194,59 @@ struct EpiPE {             // x = acc + pe[src[m] % 13]; tap = acc
 
 // ------------------------------------------------------------ kernel
 
-template <typename T, int BM, int BN, int WM, int WN, class AL, class EP>
+// Launch-site tags: one kernel symbol per call site, so profilers attribute
+// time per site.  The tag changes nothing in the generated code.
+enum Site { kQKV = 1, kFC1, kProj1, kOProj, kFC2, kProj2, kConv2, kConv3, kConvOut };
+
+template <typename T, int BM, int BN, int WM, int WN, int SITE, class AL, class EP>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __restrict__ w, int N, int K,
-                                                            int tiles_m, EP ep) {
-    constexpr int NT = WM * WN * 64;
+                                                            int tiles_m, int tiles_n, EP ep) {
+    constexpr int NW = WM * WN;               // waves
     constexpr int TM = BM / WM / 16;          // 16-row MFMA tiles per wave along M
     constexpr int TN = BN / WN / 16;          // along N
-    constexpr int PER = Elem<T>::per16;
-    constexpr int ACH = BM * 8 / NT;          // 16-byte chunks per thread per stage
-    constexpr int BCH = BN * 8 / NT;
-    static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads mismatch");
-    __shared__ __align__(16) char smem[2 * (BM + BN) * kRowBytes];
-    char* As = smem;
-    char* Bs = smem + 2 * BM * kRowBytes;
+    constexpr int PER = Elem<T>::per16;       // elements per 16-byte chunk
+    constexpr int AI = BM / (8 * NW);         // direct-to-LDS loads per wave per stage (A)
+    constexpr int BI = BN / (8 * NW);
+    constexpr int STAGE = (BM + BN) * 128;    // bytes per LDS stage
+    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile/waves mismatch");
+    __shared__ __align__(1024) char smem[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
-    const int bm = blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
+
+    // XCD-aware tile order: dispatch sends workgroup b to XCD b % 8; give each
+    // XCD a contiguous range of logical tiles, walked in groups of 8 M-tiles.
+    const int G = tiles_m * tiles_n;
+    const int b = blockIdx.x;
+    const int per_xcd = (G + 7) / 8;
+    const int xcd = b % 8, slot = b / 8;
+    const int full = G - 8 * (per_xcd - 1);   // XCDs that get per_xcd tiles (the rest get one less)
+    int t = xcd < full ? xcd * per_xcd + slot : full * per_xcd + (xcd - full) * (per_xcd - 1) + slot;
+    const int GM = 8;
+    const int group = t / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(GM, tiles_m - first_m);
+    const int in_group = t - group * GM * tiles_n;
+    const int bm = first_m + in_group % gm, bn = in_group / gm;
     const int m0 = bm * BM, n0 = bn * BN;
 
-    const int col = tid & 7;                  // 16-byte column of the 128-byte slice
-    typename AL::Ctx actx[ACH];
-    const T* wrow[BCH];
+    // this lane's rows and K-chunk for the direct-to-LDS loads
+    const int lrow = lane >> 3;               // row within the wave's 8-row block
+    const int kc = (lane & 7) ^ lrow;         // swizzled K-chunk (row % 8 == lrow)
+    // rows of this lane: A rows m0 + wave*AI*8 + lrow + 8q, weight rows likewise
+    const auto alane = al.template init<AI>(m0 + wave * AI * 8 + lrow);
+    const DenseA<T> wl{w, N, K, K};
+    const auto wlane = wl.template init<BI>(n0 + wave * BI * 8 + lrow);
+    auto issue = [&](int kt, int buf) {
+        const int k0 = kt * (8 * PER) + kc * PER;
+        const auto kx = al.kprep(k0);
+        const auto kw = wl.kprep(k0);
+        char* sa = smem + buf * STAGE + wave * AI * 1024;
+        char* sb = smem + buf * STAGE + BM * 128 + wave * BI * 1024;
 #pragma unroll
-    for (int q = 0; q < ACH; ++q) actx[q] = al.prep(m0 + tid / 8 + q * (NT / 8));
+        for (int q = 0; q < AI; ++q) dma16(al.addr(alane, q, kx), sa + q * 1024);
 #pragma unroll
-    for (int q = 0; q < BCH; ++q) {
-        const int n = n0 + tid / 8 + q * (NT / 8);
-        wrow[q] = n < N ? w + (size_t)n * K : nullptr;
-    }
-    uint4 ra[ACH], rb[BCH];
-    auto gload = [&](int kt) {
-        const int k0 = kt * (8 * PER) + col * PER;
-#pragma unroll
-        for (int q = 0; q < ACH; ++q) ra[q] = al.load(actx[q], k0);
-#pragma unroll
-        for (int q = 0; q < BCH; ++q) rb[q] = (wrow[q] && k0 < K) ? ld16(wrow[q] + k0) : zero16();
-    };
-    auto lstore = [&](int buf) {
-        char* a = As + buf * BM * kRowBytes;
-        char* b = Bs + buf * BN * kRowBytes;
-#pragma unroll
-        for (int q = 0; q < ACH; ++q) st16(a + (tid / 8 + q * (NT / 8)) * kRowBytes + col * 16, ra[q]);
-#pragma unroll
-        for (int q = 0; q < BCH; ++q) st16(b + (tid / 8 + q * (NT / 8)) * kRowBytes + col * 16, rb[q]);
+        for (int q = 0; q < BI; ++q) dma16(wl.addr(wlane, q, kw), sb + q * 1024);
     };
 
     f32x4 acc[TM][TN];
@@ -190,27 +256,60 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (K + 8 * PER - 1) / (8 * PER);
-    gload(0);
-    lstore(0);
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int fr = lane & 15, fg = lane >> 4;
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) gload(kt + 1);
-        const char* a = As + (kt & 1) * BM * kRowBytes + (wm * TM * 16 + fr) * kRowBytes + fg * 16;
-        const char* b = Bs + (kt & 1) * BN * kRowBytes + (wn * TN * 16 + fr) * kRowBytes + fg * 16;
+        if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+        const char* a = smem + (kt & 1) * STAGE + (wm * TM * 16 + fr) * 128;
+        const char* bp = smem + (kt & 1) * STAGE + BM * 128 + (wn * TN * 16 + fr) * 128;
+        // Fragments: B (weights) for a 64-byte K block stay in registers while
+        // the A fragments stream through a one-ahead prefetch; the next K
+        // block's B fragments are fetched during the last row tile.  The
+        // sched_group_barriers pin this order so every LDS read is in flight
+        // behind a full row of MFMAs instead of stalling the next one.
+        const int sw0 = ((0 + fg) ^ (fr & 7)) * 16;
+        const int sw1 = ((4 + fg) ^ (fr & 7)) * 16;
+        uint4 fb0[TN], fb1[TN];
+        uint4 fa_cur, fa_nxt;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            uint4 fa[TM], fb[TN];
+        for (int j = 0; j < TN; ++j) fb0[j] = ld16(bp + j * 16 * 128 + sw0);
+        fa_cur = ld16(a + sw0);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa[i] = ld16(a + i * 16 * kRowBytes + kb * 64);
+        for (int i = 0; i < TM; ++i) {
+            if (i + 1 < TM) {
+                fa_nxt = ld16(a + (i + 1) * 16 * 128 + sw0);
+            } else {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) fb[j] = ld16(b + j * 16 * kRowBytes + kb * 64);
+                for (int j = 0; j < TN; ++j) fb1[j] = ld16(bp + j * 16 * 128 + sw1);
+                fa_nxt = ld16(a + sw1);
+            }
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) mfma_kblock(T(), fb[j], fa[i], acc[i][j]);
+            for (int j = 0; j < TN; ++j) mfma_kblock(T(), fb0[j], fa_cur, acc[i][j]);
+            fa_cur = fa_nxt;
         }
-        if (kt + 1 < nk) lstore((kt + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i + 1 < TM) fa_nxt = ld16(a + (i + 1) * 16 * 128 + sw1);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) mfma_kblock(T(), fb1[j], fa_cur, acc[i][j]);
+            fa_cur = fa_nxt;
+        }
+        constexpr int MPK = sizeof(T) == 2 ? 1 : 4;     // MFMAs per 64-byte K block
+        __builtin_amdgcn_sched_group_barrier(0x100, TN + 1, 0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i + 1 < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x100, TN + 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, TN * MPK, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i + 1 < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, TN * MPK, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
     // acc[i][j] lane holds out[m = row fr][n = 4 fg + r] of tile (i, j)
@@ -221,12 +320,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
             ep(m0 + (wm * TM + i) * 16 + fr, n0 + (wn * TN + j) * 16 + 4 * fg, acc[i][j]);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, class AL, class EP>
+template <typename T, int BM, int BN, int WM, int WN, int SITE, class AL, class EP>
+static hipError_t launch(hipStream_t s, const AL& al, int M, const T* w, int N, int K, const EP& ep) {
+    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+    gemm_kernel<T, BM, BN, WM, WN, SITE, AL, EP><<<tm * tn, WM * WN * 64, 0, s>>>(al, w, N, K, tm, tn, ep);
+    return hipGetLastError();
+}
+
+// Tile choice: 256 x 256 with 8 waves of 128 x 64 (two waves per SIMD hide
+// LDS and MFMA latency) when the problem fills the GPU with it, else
+// 128 x 128 with 4 waves of 64 x 64.
+template <int SITE, typename T, class AL, class EP>
 static hipError_t run(hipStream_t s, const AL& al, int M, const T* w, int N, int K, const EP& ep) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    gemm_kernel<T, BM, BN, WM, WN, AL, EP><<<tm * tn, WM * WN * 64, 0, s>>>(al, w, N, K, tm, ep);
-    return hipGetLastError();
+    if (K % Elem<T>::per16) return hipErrorInvalidValue;
+    const long big = (long)((M + 255) / 256) * ((N + 255) / 256);
+    if (big >= 200) return launch<T, 256, 256, 2, 4, SITE>(s, al, M, w, N, K, ep);
+    return launch<T, 128, 128, 2, 2, SITE>(s, al, M, w, N, K, ep);
 }
 
 // ------------------------------------------------------------ entry points
@@ -238,7 +348,8 @@ hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win,
     const int M = n_chunks * Hout * Wout;
     ConvA<T> al{in, M, Hin, Win, C, Hout, Wout, time_major};
     EpiBias<T> ep{out, bias, M, C, true};
-    return run<T, 128, 128, 2, 2>(s, al, M, w, C, 9 * C, ep);
+    if (C % Elem<T>::per16) return hipErrorInvalidValue;
+    return time_major ? run<kConv3>(s, al, M, w, C, 9 * C, ep) : run<kConv2>(s, al, M, w, C, 9 * C, ep);
 }
 
 template <typename T>
@@ -246,7 +357,7 @@ hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K,
                     const float* pe, float* x, float* tap) {
     GatherA<T> al{a, src, n_tok, K};
     EpiPE ep{x, tap, pe, src, n_tok, N};
-    return run<T, 128, 128, 2, 2>(s, al, n_tok, w, N, K, ep);
+    return run<kConvOut>(s, al, n_tok, w, N, K, ep);
 }
 
 template <typename T>
@@ -254,7 +365,9 @@ hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N,
                      T* out, bool gelu) {
     DenseA<T> al{a, M, K, K};
     EpiBias<T> ep{out, bias, M, N, gelu};
-    return run<T, 128, 128, 2, 2>(s, al, M, w, N, K, ep);
+    if (!gelu) return run<kQKV>(s, al, M, w, N, K, ep);
+    if (N != K) return run<kFC1>(s, al, M, w, N, K, ep);
+    return run<kProj1>(s, al, M, w, N, K, ep);
 }
 
 template <typename T>
@@ -262,7 +375,8 @@ hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, 
                            const float* bias, float* x) {
     DenseA<T> al{a, M, K, K};
     EpiResid ep{x, bias, M, N};
-    return run<T, 128, 128, 2, 2>(s, al, M, w, N, K, ep);
+    if (N == K) return run<kOProj>(s, al, M, w, N, K, ep);
+    return run<kFC2>(s, al, M, w, N, K, ep);
 }
 
 template <typename T>
@@ -270,7 +384,7 @@ hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, in
                          const float* bias, float* out) {
     DenseA<T> al{a, M, K, K};
     EpiF32Bias ep{out, bias, M, N};
-    return run<T, 128, 128, 2, 2>(s, al, M, w, N, K, ep);
+    return run<kProj2>(s, al, M, w, N, K, ep);
 }
 
 #define QA_INST(T)                                                                                    \
