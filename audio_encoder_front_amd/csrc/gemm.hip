@@ -51,21 +51,21 @@ template <typename T>
 struct DenseA {
     const T* a;
     int M, K, lda;
-    template <int AI>
+    template <int AI, int RS>
     struct Lane { const char* base; unsigned valid; };
     struct KCtx { int off; bool ok; };
-    template <int AI>
-    __device__ Lane<AI> init(int m) const {
-        Lane<AI> l{reinterpret_cast<const char*>(a + (size_t)m * lda), 0u};
+    template <int AI, int RS>
+    __device__ Lane<AI, RS> init(int m) const {
+        Lane<AI, RS> l{reinterpret_cast<const char*>(a + (size_t)m * lda), 0u};
 #pragma unroll
-        for (int q = 0; q < AI; ++q) l.valid |= (m + 8 * q < M ? 1u : 0u) << q;
+        for (int q = 0; q < AI; ++q) l.valid |= (m + RS * q < M ? 1u : 0u) << q;
         return l;
     }
     __device__ KCtx kprep(int k0) const { return KCtx{k0 * (int)sizeof(T), k0 < K}; }
-    template <int AI>
-    __device__ const void* addr(const Lane<AI>& l, int q, const KCtx& k) const {
+    template <int AI, int RS>
+    __device__ const void* addr(const Lane<AI, RS>& l, int q, const KCtx& k) const {
         return (((l.valid >> q) & 1u) && k.ok)
-                   ? (const void*)(l.base + (size_t)q * 8 * lda * sizeof(T) + k.off)
+                   ? (const void*)(l.base + (size_t)q * RS * lda * sizeof(T) + k.off)
                    : (const void*)g_zero16;
     }
 };
@@ -75,19 +75,19 @@ struct GatherA {   // row m of the GEMM is row src[m] of a
     const T* a;
     const int* src;
     int M, K;
-    template <int AI>
+    template <int AI, int RS>
     struct Lane { int row[AI]; };
     struct KCtx { int off; bool ok; };
-    template <int AI>
-    __device__ Lane<AI> init(int m) const {
-        Lane<AI> l;
+    template <int AI, int RS>
+    __device__ Lane<AI, RS> init(int m) const {
+        Lane<AI, RS> l;
 #pragma unroll
-        for (int q = 0; q < AI; ++q) l.row[q] = m + 8 * q < M ? src[m + 8 * q] : -1;
+        for (int q = 0; q < AI; ++q) l.row[q] = m + RS * q < M ? src[m + RS * q] : -1;
         return l;
     }
     __device__ KCtx kprep(int k0) const { return KCtx{k0 * (int)sizeof(T), k0 < K}; }
-    template <int AI>
-    __device__ const void* addr(const Lane<AI>& l, int q, const KCtx& k) const {
+    template <int AI, int RS>
+    __device__ const void* addr(const Lane<AI, RS>& l, int q, const KCtx& k) const {
         return (l.row[q] >= 0 && k.ok)
                    ? (const void*)(reinterpret_cast<const char*>(a + (size_t)l.row[q] * K) + k.off)
                    : (const void*)g_zero16;
@@ -99,16 +99,16 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv over NHWC inp
     const T* in;
     int M, Hin, Win, C, Hout, Wout;
     bool time_major;                  // output row order (chunk, j, i) instead of (chunk, i, j)
-    template <int AI>
+    template <int AI, int RS>
     struct Lane { int chunk[AI]; int rc[AI]; };   // rc = (2i-1) << 16 | (2j-1) & 0xffff
     struct KCtx { int a, b, off; bool ok; };
-    template <int AI>
-    __device__ Lane<AI> init(int m0) const {
-        Lane<AI> l;
+    template <int AI, int RS>
+    __device__ Lane<AI, RS> init(int m0) const {
+        Lane<AI, RS> l;
         const int per = Hout * Wout;
 #pragma unroll
         for (int q = 0; q < AI; ++q) {
-            const int m = m0 + 8 * q;
+            const int m = m0 + RS * q;
             const int chunk = m / per, rem = m - chunk * per;
             int i, j;
             if (time_major) { j = rem / Hout; i = rem - j * Hout; }
@@ -123,8 +123,8 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv over NHWC inp
         const int a = tap / 3;
         return KCtx{a, tap - 3 * a, ci * (int)sizeof(T), tap < 9};
     }
-    template <int AI>
-    __device__ const void* addr(const Lane<AI>& l, int q, const KCtx& k) const {
+    template <int AI, int RS>
+    __device__ const void* addr(const Lane<AI, RS>& l, int q, const KCtx& k) const {
         const int r = (l.rc[q] >> 16) + k.a;
         const int col = (int)(short)(l.rc[q] & 0xffff) + k.b;
         if (l.chunk[q] < 0 || !k.ok || (unsigned)r >= (unsigned)Hin || (unsigned)col >= (unsigned)Win)
@@ -198,17 +198,29 @@ struct EpiPE {             // x = acc + pe[src[m] % 13]; tap = acc
 // time per site.  The tag changes nothing in the generated code.
 enum Site { kQKV = 1, kFC1, kProj1, kOProj, kFC2, kProj2, kConv2, kConv3, kConvOut };
 
-template <typename T, int BM, int BN, int WM, int WN, int SITE, class AL, class EP>
+// Swizzled 16-byte column of K-chunk c in LDS row r: rows of 128 B hold 8
+// chunks (XOR with r % 8), rows of 64 B hold 4 (XOR with (r / 2) % 4); either
+// way the fragment reads of 8 consecutive rows cover all 32 banks.
+template <int BKB>
+__device__ __forceinline__ int swz(int r, int c) {
+    return BKB == 128 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int BKB, int SITE, class AL, class EP>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __restrict__ w, int N, int K,
                                                             int tiles_m, int tiles_n, EP ep) {
     constexpr int NW = WM * WN;               // waves
     constexpr int TM = BM / WM / 16;          // 16-row MFMA tiles per wave along M
     constexpr int TN = BN / WN / 16;          // along N
     constexpr int PER = Elem<T>::per16;       // elements per 16-byte chunk
-    constexpr int AI = BM / (8 * NW);         // direct-to-LDS loads per wave per stage (A)
-    constexpr int BI = BN / (8 * NW);
-    constexpr int STAGE = (BM + BN) * 128;    // bytes per LDS stage
-    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile/waves mismatch");
+    constexpr int CPR = BKB / 16;             // 16-byte chunks per LDS row (per stage)
+    constexpr int RPD = 64 / CPR;             // rows filled by one direct-to-LDS load (1 KB)
+    constexpr int KB = BKB / 64;              // 64-byte MFMA K blocks per stage
+    constexpr int AI = BM / (RPD * NW);       // direct-to-LDS loads per wave per stage (A)
+    constexpr int BI = BN / (RPD * NW);
+    constexpr int STAGE = (BM + BN) * BKB;    // bytes per LDS stage
+    static_assert(BM % (RPD * NW) == 0 && BN % (RPD * NW) == 0, "tile/waves mismatch");
+    static_assert(TN >= 3, "the two-ahead weight prefetch needs at least 3 weight tiles");
     __shared__ __align__(1024) char smem[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -230,19 +242,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     const int bm = first_m + in_group % gm, bn = in_group / gm;
     const int m0 = bm * BM, n0 = bn * BN;
 
-    // this lane's rows and K-chunk for the direct-to-LDS loads
-    const int lrow = lane >> 3;               // row within the wave's 8-row block
-    const int kc = (lane & 7) ^ lrow;         // swizzled K-chunk (row % 8 == lrow)
-    // rows of this lane: A rows m0 + wave*AI*8 + lrow + 8q, weight rows likewise
-    const auto alane = al.template init<AI>(m0 + wave * AI * 8 + lrow);
+    // This lane's rows and K-chunk for the direct-to-LDS loads: a load fills
+    // 1 KB = RPD rows of BKB bytes, lane l landing in row l / CPR, column
+    // l % CPR, so it fetches the chunk that the swizzle puts there.
+    const int lrow = lane / CPR;
+    const int kc = swz<BKB>(lrow, lane % CPR);
+    const auto alane = al.template init<AI, RPD>(m0 + wave * AI * RPD + lrow);
     const DenseA<T> wl{w, N, K, K};
-    const auto wlane = wl.template init<BI>(n0 + wave * BI * 8 + lrow);
+    const auto wlane = wl.template init<BI, RPD>(n0 + wave * BI * RPD + lrow);
+    constexpr int KSTEP = BKB / (int)sizeof(T);   // K elements per stage
     auto issue = [&](int kt, int buf) {
-        const int k0 = kt * (8 * PER) + kc * PER;
+        const int k0 = kt * KSTEP + kc * PER;
         const auto kx = al.kprep(k0);
         const auto kw = wl.kprep(k0);
         char* sa = smem + buf * STAGE + wave * AI * 1024;
-        char* sb = smem + buf * STAGE + BM * 128 + wave * BI * 1024;
+        char* sb = smem + buf * STAGE + BM * BKB + wave * BI * 1024;
 #pragma unroll
         for (int q = 0; q < AI; ++q) dma16(al.addr(alane, q, kx), sa + q * 1024);
 #pragma unroll
@@ -255,59 +269,59 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = (K + 8 * PER - 1) / (8 * PER);
+    const int nk = (K + KSTEP - 1) / KSTEP;
     issue(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int fr = lane & 15, fg = lane >> 4;
+    int sw[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sw[kb] = swz<BKB>(fr, kb * 4 + fg) * 16;
+    constexpr int MPK = sizeof(T) == 2 ? 1 : 4;   // MFMAs per 64-byte K block
     for (int kt = 0; kt < nk; ++kt) {
         if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-        const char* a = smem + (kt & 1) * STAGE + (wm * TM * 16 + fr) * 128;
-        const char* bp = smem + (kt & 1) * STAGE + BM * 128 + (wn * TN * 16 + fr) * 128;
-        // Fragments: B (weights) for a 64-byte K block stay in registers while
-        // the A fragments stream through a one-ahead prefetch; the next K
-        // block's B fragments are fetched during the last row tile.  The
-        // sched_group_barriers pin this order so every LDS read is in flight
-        // behind a full row of MFMAs instead of stalling the next one.
-        const int sw0 = ((0 + fg) ^ (fr & 7)) * 16;
-        const int sw1 = ((4 + fg) ^ (fr & 7)) * 16;
-        uint4 fb0[TN], fb1[TN];
-        uint4 fa_cur, fa_nxt;
+        const char* a = smem + (kt & 1) * STAGE + (wm * TM * 16 + fr) * BKB;
+        const char* bp = smem + (kt & 1) * STAGE + BM * BKB + (wn * TN * 16 + fr) * BKB;
+        // Fragments: the TM activation fragments of a 64-byte K block stay in
+        // registers while the TN weight fragments stream through a two-ahead
+        // prefetch; the next K block's activation fragments are fetched during
+        // the current block's third-from-last weight tile.  The
+        // sched_group_barriers pin this order, so each LDS read has two MFMA
+        // groups (2 TM MFMAs) to land.
+        uint4 fa[KB][TM], fb[KB][TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb0[j] = ld16(bp + j * 16 * 128 + sw0);
-        fa_cur = ld16(a + sw0);
+        for (int i = 0; i < TM; ++i) fa[0][i] = ld16(a + i * 16 * BKB + sw[0]);
+        fb[0][0] = ld16(bp + sw[0]);
+        fb[0][1] = ld16(bp + 16 * BKB + sw[0]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i + 1 < TM) {
-                fa_nxt = ld16(a + (i + 1) * 16 * 128 + sw0);
-            } else {
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j) fb1[j] = ld16(bp + j * 16 * 128 + sw1);
-                fa_nxt = ld16(a + sw1);
+            for (int j = 0; j < TN; ++j) {
+                if (j + 2 < TN) {
+                    fb[kb][j + 2] = ld16(bp + (j + 2) * 16 * BKB + sw[kb]);
+                } else if (kb + 1 < KB) {
+                    if (j + 2 == TN) {
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) fa[kb + 1][i] = ld16(a + i * 16 * BKB + sw[kb + 1]);
+                        fb[kb + 1][0] = ld16(bp + sw[kb + 1]);
+                    } else {
+                        fb[kb + 1][1] = ld16(bp + 16 * BKB + sw[kb + 1]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i) mfma_kblock(T(), fb[kb][j], fa[kb][i], acc[i][j]);
             }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) mfma_kblock(T(), fb0[j], fa_cur, acc[i][j]);
-            fa_cur = fa_nxt;
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, TM + 2, 0);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i + 1 < TM) fa_nxt = ld16(a + (i + 1) * 16 * 128 + sw1);
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) mfma_kblock(T(), fb1[j], fa_cur, acc[i][j]);
-            fa_cur = fa_nxt;
-        }
-        constexpr int MPK = sizeof(T) == 2 ? 1 : 4;     // MFMAs per 64-byte K block
-        __builtin_amdgcn_sched_group_barrier(0x100, TN + 1, 0);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i + 1 < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            else __builtin_amdgcn_sched_group_barrier(0x100, TN + 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, TN * MPK, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i + 1 < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, TN * MPK, 0);
+            for (int j = 0; j < TN; ++j) {
+                if (j + 2 < TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                else if (kb + 1 < KB && j + 2 == TN) __builtin_amdgcn_sched_group_barrier(0x100, TM + 1, 0);
+                else if (kb + 1 < KB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, TM * MPK, 0);
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -320,10 +334,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
             ep(m0 + (wm * TM + i) * 16 + fr, n0 + (wn * TN + j) * 16 + 4 * fg, acc[i][j]);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int SITE, class AL, class EP>
+template <typename T, int BM, int BN, int WM, int WN, int BKB, int SITE, class AL, class EP>
 static hipError_t launch(hipStream_t s, const AL& al, int M, const T* w, int N, int K, const EP& ep) {
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    gemm_kernel<T, BM, BN, WM, WN, SITE, AL, EP><<<tm * tn, WM * WN * 64, 0, s>>>(al, w, N, K, tm, tn, ep);
+    gemm_kernel<T, BM, BN, WM, WN, BKB, SITE, AL, EP><<<tm * tn, WM * WN * 64, 0, s>>>(al, w, N, K, tm, tn, ep);
     return hipGetLastError();
 }
 
@@ -335,8 +349,8 @@ static hipError_t run(hipStream_t s, const AL& al, int M, const T* w, int N, int
     if (M <= 0 || N <= 0) return hipSuccess;
     if (K % Elem<T>::per16) return hipErrorInvalidValue;
     const long big = (long)((M + 255) / 256) * ((N + 255) / 256);
-    if (big >= 200) return launch<T, 256, 256, 2, 4, SITE>(s, al, M, w, N, K, ep);
-    return launch<T, 128, 128, 2, 2, SITE>(s, al, M, w, N, K, ep);
+    if (big >= 200) return launch<T, 256, 256, 2, 4, 128, SITE>(s, al, M, w, N, K, ep);
+    return launch<T, 128, 128, 2, 2, 128, SITE>(s, al, M, w, N, K, ep);
 }
 
 // ------------------------------------------------------------ entry points

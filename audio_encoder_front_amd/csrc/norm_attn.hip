@@ -136,24 +136,32 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     const int s0 = cu[win], n = cu[win + 1] - s0;
     const int tid = threadIdx.x;
     const size_t ld = 3 * (size_t)d;
-    // Q, K rows (zero beyond n)
-    for (int idx = tid; idx < kMaxWindow * CPR; idx += 256) {
+    // Q, K, V rows of this head, 16 bytes per load, all loads issued before
+    // any LDS store (rows at or beyond n are zeros).  V is written transposed.
+    constexpr int NCH = kMaxWindow * CPR / 256;    // 16-byte chunks per thread per matrix
+    uint4 qv[NCH], kv[NCH], vv[NCH];
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+        const int idx = tid + q * 256;
         const int t = idx / CPR, c = idx % CPR;
-        uint4 qv = zero16(), kv = zero16();
+        qv[q] = kv[q] = vv[q] = zero16();
         if (t < n) {
             const T* row = qkv + (size_t)(s0 + t) * ld + h * kHd + c * PER;
-            qv = ld16(row);
-            kv = ld16(row + d);
+            qv[q] = ld16(row);
+            kv[q] = ld16(row + d);
+            vv[q] = ld16(row + 2 * d);
         }
-        st16(qs + t * QR + c * 16, qv);
-        st16(ks + t * QR + c * 16, kv);
     }
-    // V^T[dd][t] (zero beyond n)
-    for (int idx = tid; idx < kMaxWindow * kHd; idx += 256) {
-        const int t = idx / kHd, dd = idx % kHd;
-        T v = from_f32<T>(0.f);
-        if (t < n) v = qkv[(size_t)(s0 + t) * ld + 2 * d + h * kHd + dd];
-        *reinterpret_cast<T*>(vts + dd * VR + t * sizeof(T)) = v;
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+        const int idx = tid + q * 256;
+        const int t = idx / CPR, c = idx % CPR;
+        st16(qs + t * QR + c * 16, qv[q]);
+        st16(ks + t * QR + c * 16, kv[q]);
+        const T* ve = reinterpret_cast<const T*>(&vv[q]);
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            *reinterpret_cast<T*>(vts + (c * PER + e) * VR + t * sizeof(T)) = ve[e];
     }
     __syncthreads();
 

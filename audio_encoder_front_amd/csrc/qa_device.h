@@ -37,8 +37,26 @@ __device__ __forceinline__ void mfma_kblock(float, const uint4& a, const uint4& 
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-// Exact (erf) GELU.
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
+// exp(-x^2) with t = 1 / (1 + p x); absolute error <= 1.5e-7; odd extension
+// for x < 0.  Branch-free: one reciprocal, one exp2, five FMAs.
+__device__ __forceinline__ float erf_as7126(float x) {
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+    float y = fmaf(1.061405429f, t, -1.453152027f);
+    y = fmaf(y, t, 1.421413741f);
+    y = fmaf(y, t, -0.284496736f);
+    y = fmaf(y, t, 0.254829592f);
+    y *= t;
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * ax * ax);   // exp(-x^2)
+    return copysignf(fmaf(-y, e, 1.0f), x);
+}
+
+// GELU with the erf (not tanh) form: x * (1 + erf(x / sqrt 2)) / 2.
+__device__ __forceinline__ float gelu_erf(float x) {
+    return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f));
+}
 
 // Store 4 consecutive values (fp32 -> 16 bytes, bf16 -> 8 bytes, RNE).
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
