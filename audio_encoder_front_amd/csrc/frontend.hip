@@ -8,7 +8,7 @@
 // reflection, Slaney mel, power floor 1e-10, log10 peak-minus-eight, (x+4)/4,
 // floor(len/160) frames).
 //
-// Kernel design (one wave per 64-frame tile):
+// Kernel design (two waves per 64-frame tile, splitting the DFT bins):
 //  * the tile's samples (with mirror padding) sit in LDS, two pad words every
 //    160 samples so that the 16 frames x 4 samples a fragment reads fall in
 //    distinct banks;
@@ -19,7 +19,9 @@
 //  * the lane layout of D is exactly the A-operand layout GEMM 2 needs
 //    (frame = lane%16, bin = 4*(lane/16) + r at k-step r), so the power feeds
 //    the mel MFMA straight from registers;
-//  * mel tiles with no nonzero filter weight for a bin block are skipped.
+//  * mel tiles with no nonzero filter weight for a bin block are skipped;
+//  * the two waves take alternate 16-bin blocks; their partial mel energies
+//    meet in LDS (the sample buffer is free by then) before the log.
 #include "qa_device.h"
 #include "qa_kernels.h"
 
@@ -36,7 +38,7 @@ __global__ void init_flags_kernel(int* clip_key, int n_clips, int* flag) {
     if (i == 0) *flag = 0;
 }
 
-__global__ __launch_bounds__(64) void frontend_kernel(
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void frontend_kernel(
     const float* __restrict__ pcm, const ClipInfo* __restrict__ clips,
     const FrontTile* __restrict__ tiles, const float* __restrict__ basis,
     const float* __restrict__ fbB, const int* __restrict__ fb_range,
@@ -46,10 +48,10 @@ __global__ __launch_bounds__(64) void frontend_kernel(
     const ClipInfo c = clips[t.clip];
     const float* x = pcm + c.sample_off;
     const int L = c.len;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nsamp = 160 * (t.nframes - 1) + 400;
     bool bad = false;
-    for (int s = lane; s < kSpan; s += 64) {
+    for (int s = threadIdx.x; s < kSpan; s += 128) {
         float v = 0.0f;
         if (s < nsamp) {
             int i = 160 * t.frame0 + s - 200;     // centered: frame j starts 200 samples early
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(64) void frontend_kernel(
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft) fbase[ft] = 162 * (ft * 16 + li);   // pad_index(160*frame)
 
-    for (int bc = 0; bc < kBinChunks; ++bc) {
+    for (int bc = wave; bc < kBinChunks; bc += 2) {
         f32x4 re[4], im[4];
 #pragma unroll
         for (int ft = 0; ft < 4; ++ft) { re[ft] = f32x4{0.f, 0.f, 0.f, 0.f}; im[ft] = re[ft]; }
@@ -107,6 +109,29 @@ __global__ __launch_bounds__(64) void frontend_kernel(
             }
         }
     }
+
+    // combine the two waves' partial mel energies through LDS
+    __syncthreads();
+    float4* ex = reinterpret_cast<float4*>(xs);
+    if (wave == 1) {
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                ex[(ft * 8 + mt) * 64 + lane] = make_float4(E[ft][mt][0], E[ft][mt][1], E[ft][mt][2], E[ft][mt][3]);
+    }
+    __syncthreads();
+    if (wave == 1) {
+        if (__any(bad) && lane == 0) atomicOr(flag, 1);
+        return;
+    }
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const float4 o = ex[(ft * 8 + mt) * 64 + lane];
+            E[ft][mt][0] += o.x; E[ft][mt][1] += o.y; E[ft][mt][2] += o.z; E[ft][mt][3] += o.w;
+        }
 
     // E[ft][mt] lane holds mel energy of frame ft*16 + 4g + r, mel mt*16 + li.
     float vmax = -INFINITY;
@@ -162,7 +187,7 @@ hipError_t frontend(hipStream_t s, const float* pcm, const ClipInfo* clips, cons
                     int n_tiles, const float* basis, const float* fbB, const int* fb_range,
                     float* logmel, int* clip_key, int* flag) {
     if (n_tiles <= 0) return hipSuccess;
-    frontend_kernel<<<n_tiles, 64, 0, s>>>(pcm, clips, tiles, basis, fbB, fb_range, logmel, clip_key, flag);
+    frontend_kernel<<<n_tiles, 128, 0, s>>>(pcm, clips, tiles, basis, fbB, fb_range, logmel, clip_key, flag);
     return hipGetLastError();
 }
 

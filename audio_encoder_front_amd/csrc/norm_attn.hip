@@ -128,35 +128,48 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     constexpr int QR = AttnLds<T>::qrow, VR = AttnLds<T>::vrow;
     constexpr int PER = Elem<T>::per16;
     constexpr int CPR = kHd / PER;                 // 16-byte chunks per head row
-    __shared__ __align__(16) char qs[kMaxWindow * QR];
+    constexpr int KBN = kHd * (int)sizeof(T) / 64; // 64-byte MFMA K blocks per head row
     __shared__ __align__(16) char ks[kMaxWindow * QR];
     __shared__ __align__(16) char vts[kHd * VR];
 
     const int win = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
     const int s0 = cu[win], n = cu[win + 1] - s0;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int nt = (n + 15) >> 4;                  // 16-row tiles in this window
     const size_t ld = 3 * (size_t)d;
-    // Q, K, V rows of this head, 16 bytes per load, all loads issued before
-    // any LDS store (rows at or beyond n are zeros).  V is written transposed.
+
+    // Query fragments of this wave's first tile come straight from global
+    // memory (B operand: lane holds query row fr, K chunk fg of each block).
+    auto load_q = [&](int qt, uint4* qf) {
+        const int q = qt * 16 + fr;
+        const T* row = qkv + (size_t)(s0 + q) * ld + h * kHd + fg * PER;
+#pragma unroll
+        for (int kb = 0; kb < KBN; ++kb) qf[kb] = q < n ? ld16(row + kb * (64 / (int)sizeof(T))) : zero16();
+    };
+    uint4 qf[KBN];
+    if (wave < nt) load_q(wave, qf);
+
+    // K and V rows of this head (16 bytes per load, every load issued before
+    // any LDS store); rows at or beyond n are zeros.  V is stored transposed.
     constexpr int NCH = kMaxWindow * CPR / 256;    // 16-byte chunks per thread per matrix
-    uint4 qv[NCH], kv[NCH], vv[NCH];
+    uint4 kv[NCH], vv[NCH];
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
         const int idx = tid + q * 256;
         const int t = idx / CPR, c = idx % CPR;
-        qv[q] = kv[q] = vv[q] = zero16();
+        kv[q] = vv[q] = zero16();
         if (t < n) {
-            const T* row = qkv + (size_t)(s0 + t) * ld + h * kHd + c * PER;
-            qv[q] = ld16(row);
-            kv[q] = ld16(row + d);
-            vv[q] = ld16(row + 2 * d);
+            const T* row = qkv + (size_t)(s0 + t) * ld + d + h * kHd + c * PER;
+            kv[q] = ld16(row);
+            vv[q] = ld16(row + d);
         }
     }
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
         const int idx = tid + q * 256;
         const int t = idx / CPR, c = idx % CPR;
-        st16(qs + t * QR + c * 16, qv[q]);
         st16(ks + t * QR + c * 16, kv[q]);
         const T* ve = reinterpret_cast<const T*>(&vv[q]);
 #pragma unroll
@@ -165,26 +178,21 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     }
     __syncthreads();
 
-    const int lane = tid & 63, wave = tid >> 6;
-    const int fr = lane & 15, fg = lane >> 4;
-    const int nt = (n + 15) >> 4;                  // 16-row tiles in this window
     const float sc = 0.125f * 1.4426950408889634f; // 1/sqrt(64) * log2(e)
     for (int qt = wave; qt < nt; qt += 4) {
         f32x4 sacc[8];
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const char* qrow = qs + (qt * 16 + fr) * QR + fg * 16;
 #pragma unroll
-        for (int kb = 0; kb < kHd * (int)sizeof(T) / 64; ++kb) {
-            const uint4 qf = ld16(qrow + kb * 64);
+        for (int kb = 0; kb < KBN; ++kb) {
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
-                if (kt < nt) {
-                    const uint4 kf = ld16(ks + (kt * 16 + fr) * QR + fg * 16 + kb * 64);
-                    mfma_kblock(T(), kf, qf, sacc[kt]);
-                }
+            for (int kt = 0; kt < 8; ++kt) {   // all 8 key tiles: rows past n are zeros, masked below
+                const uint4 kf = ld16(ks + (kt * 16 + fr) * QR + fg * 16 + kb * 64);
+                mfma_kblock(T(), kf, qf[kb], sacc[kt]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (qt + 4 < nt) load_q(qt + 4, qf);       // next tile's queries, in flight during softmax and P.V
         // sacc[kt][r] = score(key kt*16 + 4fg + r, query qt*16 + fr)
         float mx = -INFINITY;
 #pragma unroll
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = kt * 16 + 4 * fg + r;
-                const float v = (kt < nt && key < n) ? sacc[kt][r] * sc : -INFINITY;
+                const float v = key < n ? sacc[kt][r] * sc : -INFINITY;
                 sacc[kt][r] = v;
                 mx = fmaxf(mx, v);
             }
@@ -214,12 +222,16 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
         for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (sizeof(T) == 2) {
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-                if (2 * st < nt) pv_step(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+            for (int st = 0; st < 4; ++st) {   // keys past n have p = 0 and zero V rows
+                pv_step(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         } else {
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
-                if (kt < nt) pv_step(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
+            for (int kt = 0; kt < 8; ++kt) {
+                pv_step(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         const int q = qt * 16 + fr;
         if (q < n) {

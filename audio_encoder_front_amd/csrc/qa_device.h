@@ -67,6 +67,15 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
     bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
     *reinterpret_cast<bf16x4*>(p) = v;
 }
+// Store 8 consecutive values (bf16: one 16-byte store).
+__device__ __forceinline__ void store8(float* p, const float* v) {
+    store4(p, v[0], v[1], v[2], v[3]);
+    store4(p + 4, v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(bf16* p, const float* v) {
+    bf16x8 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3], (bf16)v[4], (bf16)v[5], (bf16)v[6], (bf16)v[7]};
+    *reinterpret_cast<bf16x8*>(p) = o;
+}
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
 template <typename T> __device__ __forceinline__ T from_f32(float v);

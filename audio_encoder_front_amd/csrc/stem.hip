@@ -68,9 +68,9 @@ __global__ __launch_bounds__(256) void conv1_kernel(const float* __restrict__ lo
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[q] = fmaf(w[a * 3 + bb][q], v, acc[q]);
             }
-        T* o = obase + ((size_t)i * kC1Wout + j) * C + c0;
-        store4(o, gelu_erf(acc[0]), gelu_erf(acc[1]), gelu_erf(acc[2]), gelu_erf(acc[3]));
-        store4(o + 4, gelu_erf(acc[4]), gelu_erf(acc[5]), gelu_erf(acc[6]), gelu_erf(acc[7]));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = gelu_erf(acc[q]);
+        store8(obase + ((size_t)i * kC1Wout + j) * C + c0, acc);
     }
 }
 
