@@ -24,7 +24,7 @@ CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=gfx950",
     # packed fp32 VALU ops stay off: the compiler emits plain fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -37,8 +37,16 @@ __device__ __align__(16) uint4 g_zero16[2];
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// global_load_lds_dwordx4 written as inline asm: the compiler's wait-count
+// pass cannot tell the two LDS stages apart and would otherwise wait for the
+// in-flight stage k+1 loads before every LDS read of stage k.  Completion is
+// awaited explicitly (s_waitcnt vmcnt(0)) before the barrier that publishes
+// a stage.  M0 carries the wave's LDS destination; no other code in these
+// kernels uses M0.
 __device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_wave_base, 16, 0, 0);
+    const unsigned base = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(lds_void*)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "m0");
 }
 
 // ------------------------------------------------------------ A loaders
@@ -279,7 +287,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     for (int kb = 0; kb < KB; ++kb) sw[kb] = swz<BKB>(fr, kb * 4 + fg) * 16;
     constexpr int MPK = sizeof(T) == 2 ? 1 : 4;   // MFMAs per 64-byte K block
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+        // Loads of the next stage (past the last stage they fetch zeros into
+        // the idle buffer), kept in this basic block so that the scheduling
+        // below can spread them between the MFMA groups.
+        issue(kt + 1, (kt + 1) & 1);
         const char* a = smem + (kt & 1) * STAGE + (wm * TM * 16 + fr) * BKB;
         const char* bp = smem + (kt & 1) * STAGE + BM * BKB + (wn * TN * 16 + fr) * BKB;
         // Fragments: the TM activation fragments of a 64-byte K block stay in
@@ -312,6 +323,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
                 for (int i = 0; i < TM; ++i) mfma_kblock(T(), fb[kb][j], fa[kb][i], acc[i][j]);
             }
         }
+        // One MFMA group per weight tile; the next stage's direct-to-LDS loads
+        // are dealt out over the groups so they never issue as a burst.
+        constexpr int VPG = (AI + BI + KB * TN - 1) / (KB * TN);
         __builtin_amdgcn_sched_group_barrier(0x100, TM + 2, 0);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -320,6 +334,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
                 if (j + 2 < TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 else if (kb + 1 < KB && j + 2 == TN) __builtin_amdgcn_sched_group_barrier(0x100, TM + 1, 0);
                 else if (kb + 1 < KB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, VPG, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, TM * MPK, 0);
             }
         }
