@@ -335,13 +335,16 @@ QA_API qa_encoder* qa_encoder_create(const qa_weights* w, const qa_dims* d) {
         e->conv1_w = put_f32(r);
         e->conv1_b = put_f32(f32vec(w->conv1_b, C));
     }
-    // conv2/conv3 [Co][Ci][3][3] -> [Co][(a*3+b)*C + ci]
+    // conv2/conv3 [Co][Ci][3][3] -> [Co][K], K index (ci / 32, tap, ci % 32)
     auto conv_pack = [&](const void* p) {
         auto v = f32vec(p, (size_t)C * C * 9);
         std::vector<float> r((size_t)C * 9 * C);
+        const int cb = qa::kConvCB;
         for (int co = 0; co < C; ++co)
             for (int ci = 0; ci < C; ++ci)
-                for (int k = 0; k < 9; ++k) r[((size_t)co * 9 + k) * C + ci] = v[((size_t)co * C + ci) * 9 + k];
+                for (int k = 0; k < 9; ++k)
+                    r[(size_t)co * 9 * C + (size_t)(ci / cb) * 9 * cb + k * cb + ci % cb] =
+                        v[((size_t)co * C + ci) * 9 + k];
         return put_op(r);
     };
     e->conv2_w = conv_pack(w->conv2_w);

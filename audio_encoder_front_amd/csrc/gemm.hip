@@ -126,10 +126,14 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv over NHWC inp
         }
         return l;
     }
+    // K order (channel block of 32, tap, channel in block): the 9 taps of a
+    // 32-channel slab are consecutive K stages, so the input slab a tile
+    // gathers is reused from L2 before the next slab is fetched.
     __device__ KCtx kprep(int k0) const {
-        const int tap = k0 / C, ci = k0 - tap * C;
+        const int cb = k0 / (9 * kConvCB), rem = k0 - cb * (9 * kConvCB);
+        const int tap = rem / kConvCB, ci = cb * kConvCB + (rem - tap * kConvCB);
         const int a = tap / 3;
-        return KCtx{a, tap - 3 * a, ci * (int)sizeof(T), tap < 9};
+        return KCtx{a, tap - 3 * a, ci * (int)sizeof(T), k0 < 9 * C};
     }
     template <int AI, int RS>
     __device__ const void* addr(const Lane<AI, RS>& l, int q, const KCtx& k) const {

@@ -37,6 +37,7 @@ constexpr int kBinChunks = 13;       // 13 x 16 = 208 >= 201 DFT bins
 constexpr int kChunk = 100;          // frames per conv chunk
 constexpr int kChunkTok = 13;        // tokens per full chunk
 constexpr int kMaxWindow = 128;      // attention kernel capacity (tokens per window)
+constexpr int kConvCB = 32;          // input-channel block of the conv2/conv3 K order
 
 // ---- front end
 hipError_t init_flags(hipStream_t s, int* clip_key, int n_clips, int* flag);
@@ -51,7 +52,7 @@ template <typename T>
 hipError_t conv1(hipStream_t s, const float* logmel, const ChunkInfo* chunks, int n_chunks,
                  const float* w9c, const float* bias, int C, T* out);
 // conv 3x3 stride 2 pad 1 over NHWC input [n_chunks][Hin][Win][C] as an
-// implicit GEMM; weights [C_out][9*C] with k = (a*3+b)*C + ci.  Output is
+// implicit GEMM; weights [C_out][9*C] with k = (ci/32)*288 + (a*3+b)*32 + ci%32.  Output is
 // [n_chunks][Hout][Wout][C] (time_major=false) or [n_chunks][Wout][Hout][C].
 template <typename T>
 hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win, int C,

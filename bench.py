@@ -67,6 +67,44 @@ def kernel_work(d, lengths):
     return work, (ch, T, fr, wins)
 
 
+# Source files whose kernels the HBM-traffic figure in profiles/ was taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "b17_20m_traffic.json")
+KERNEL_SOURCES = ["audio_encoder_front_amd/csrc/gemm.hip", "audio_encoder_front_amd/csrc/qa_device.h",
+                  "audio_encoder_front_amd/csrc/qa_kernels.h"]
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE measurement, or None if there is none for this
+    kernel and workload or the kernel sources changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("kernel") != kernel or rec.get("sources") != sources_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration(nbytes: int = 1 << 30):
+    """One plain device-to-device copy of nbytes, the reference the HBM
+    traffic counters are scaled against."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(wl, seconds: float):
     """The fp64 oracle on the first `seconds` of the workload's first clip."""
     import numpy as np
@@ -96,6 +134,8 @@ def main():
     ap.add_argument("--workload", default="b17_20m")
     ap.add_argument("--cpu-sample-s", type=float, default=240.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the encoder runs on a single MI355X and this build has no "
@@ -157,7 +197,7 @@ def main():
         peak = PEAK_BF16_TFLOPS if kind == "bf16" else PEAK_FP32_MFMA_TFLOPS
         roof = {"bound": "mfma", "achieved": f / avg_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, wl.name)
     roof["kernel"] = dom
     roof["per_launch"] = {"flops": f, "bytes": b}
     res = {
@@ -180,6 +220,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if args.calibrate_copy:
+        copy_calibration()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_s)
     enc.free()
