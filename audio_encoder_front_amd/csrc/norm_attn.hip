@@ -8,6 +8,8 @@
 // request, all in one packed ragged batch (cu_seqlens).  OneSpeech "Front end
 // and graph numerics": scores and softmax stay fp32, the attended output is
 // rounded to bf16.
+#include <algorithm>
+
 #include "qa_device.h"
 #include "qa_kernels.h"
 
@@ -27,40 +29,56 @@ template <typename T>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, int M, int d,
                                                         const float* __restrict__ g,
                                                         const float* __restrict__ b, T* __restrict__ out) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // Each wave walks rows row0, row0 + stride, ...; the next row's loads are
+    // issued before the current row is reduced, keeping two rows in flight.
     const int lane = threadIdx.x & 63;
-    if (row >= M) return;
+    const int stride = gridDim.x * 4;
     const int d4 = d >> 2;
-    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * d);
-    float4 v[8];
-    float s = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int i = lane + 64 * q;
-        if (i < d4) { v[q] = xr[i]; s += (v[q].x + v[q].y) + (v[q].z + v[q].w); }
-    }
-    const float mean = wave_sum(s) / (float)d;
-    float ss = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int i = lane + 64 * q;
-        if (i < d4) {
-            const float a = v[q].x - mean, bb = v[q].y - mean, c = v[q].z - mean, e = v[q].w - mean;
-            ss += (a * a + bb * bb) + (c * c + e * e);
-        }
-    }
-    const float rstd = rsqrtf(wave_sum(ss) / (float)d + kLnEps);
     const float4* g4 = reinterpret_cast<const float4*>(g);
     const float4* b4 = reinterpret_cast<const float4*>(b);
-    T* o = out + (size_t)row * d;
+    auto load_row = [&](int row, float4* v) {
+        const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * d);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int i = lane + 64 * q;
-        if (i < d4) {
-            const float4 gg = g4[i], bb = b4[i];
-            store4(o + 4 * i, (v[q].x - mean) * rstd * gg.x + bb.x, (v[q].y - mean) * rstd * gg.y + bb.y,
-                   (v[q].z - mean) * rstd * gg.z + bb.z, (v[q].w - mean) * rstd * gg.w + bb.w);
+        for (int q = 0; q < 8; ++q) {
+            const int i = lane + 64 * q;
+            if (i < d4) v[q] = xr[i];
         }
+    };
+    int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    float4 cur[8], nxt[8];
+    load_row(row, cur);
+    for (; row < M; row += stride) {
+        if (row + stride < M) load_row(row + stride, nxt);
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int i = lane + 64 * q;
+            if (i < d4) s += (cur[q].x + cur[q].y) + (cur[q].z + cur[q].w);
+        }
+        const float mean = wave_sum(s) / (float)d;
+        float ss = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int i = lane + 64 * q;
+            if (i < d4) {
+                const float a = cur[q].x - mean, bb = cur[q].y - mean, c = cur[q].z - mean, e = cur[q].w - mean;
+                ss += (a * a + bb * bb) + (c * c + e * e);
+            }
+        }
+        const float rstd = rsqrtf(wave_sum(ss) / (float)d + kLnEps);
+        T* o = out + (size_t)row * d;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int i = lane + 64 * q;
+            if (i < d4) {
+                const float4 gg = g4[i], bb = b4[i];
+                store4(o + 4 * i, (cur[q].x - mean) * rstd * gg.x + bb.x, (cur[q].y - mean) * rstd * gg.y + bb.y,
+                       (cur[q].z - mean) * rstd * gg.z + bb.z, (cur[q].w - mean) * rstd * gg.w + bb.w);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
     }
 }
 
@@ -68,7 +86,8 @@ template <typename T>
 hipError_t layernorm(hipStream_t s, const float* x, int M, int d, const float* g, const float* b, T* out) {
     if (M <= 0) return hipSuccess;
     if (d % 4 || d > 2048) return hipErrorInvalidValue;
-    layernorm_kernel<T><<<(M + 3) / 4, 256, 0, s>>>(x, M, d, g, b, out);
+    const int blocks = std::min((M + 3) / 4, 256 * 4);   // four waves per SIMD, each walking rows
+    layernorm_kernel<T><<<blocks, 256, 0, s>>>(x, M, d, g, b, out);
     return hipGetLastError();
 }
 
