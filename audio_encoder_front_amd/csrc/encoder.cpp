@@ -42,6 +42,7 @@ void set_err(const char* fmt, ...) {
 }
 
 constexpr int64_t kMaxSamples = 20LL * 60 * 16000;   // a request hears up to 20 minutes
+constexpr int64_t kMaxFullInput = 30LL * 16000;      // bounded input of full-input attention (30 s)
 constexpr int kHop = 160;
 constexpr int kNfft = 400;
 constexpr int kBins = kNfft / 2 + 1;
@@ -237,8 +238,8 @@ bool check_dims(const qa_dims* d) {
     if (d->n_mels != 128) { set_err("n_mels must be 128"); return false; }
     if (d->chunk_frames != 100) { set_err("chunk_frames must be 100"); return false; }
     if (d->head_dim != 64) { set_err("head_dim must be 64"); return false; }
-    if (d->window_chunks < 1 || d->window_chunks * qa::kChunkTok > qa::kMaxWindow) {
-        set_err("window_chunks must be in 1..%d", qa::kMaxWindow / qa::kChunkTok);
+    if (d->window_chunks < 0 || d->window_chunks * qa::kChunkTok > qa::kMaxWindow) {
+        set_err("window_chunks must be 0 (full-input attention) or in 1..%d", qa::kMaxWindow / qa::kChunkTok);
         return false;
     }
     if (d->conv_channels < 32 || d->conv_channels > 1024 || d->conv_channels % 32) {
@@ -492,7 +493,8 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     std::vector<int> tok_src, cu{0};
     int64_t sample_off = 0;
     int64_t frame_row = 0;
-    const int win_tok = d.window_chunks * qa::kChunkTok;
+    // window_chunks == 0: one attention segment per clip (full-input attention)
+    const int win_tok = d.window_chunks > 0 ? d.window_chunks * qa::kChunkTok : (1 << 30);
     for (int i = 0; i < n_clips; ++i) {
         const int64_t len = lengths[i];
         const int nf = (int)(len / kHop);
@@ -513,6 +515,8 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     }
     const int n_frames = (int)frame_row, n_chunks = (int)chunks.size(), n_tok = (int)tok_src.size();
     const int n_win = (int)cu.size() - 1, n_tiles = (int)tiles.size();
+    int max_seg = 0;
+    for (int i = 0; i < n_win; ++i) max_seg = std::max(max_seg, cu[i + 1] - cu[i]);
     if (n_tok > 0 && !out) { set_err("out is NULL but the batch has %d tokens", n_tok); return QA_STATUS_INVALID_PARAMS; }
     if (sample_off > 0 && !pcm) { set_err("pcm is NULL"); return QA_STATUS_INVALID_PARAMS; }
     if (n_tok == 0) {
@@ -634,7 +638,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
         const LayerW& lw = e->layers[l];
         QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b), h));
         QA_LAUNCH("qkv", qa::gemm_bias<T>(s, h, n_tok, D, e->W<T>(lw.qkv_w), 3 * D, e->W<float>(lw.qkv_b), qkv, false));
-        QA_LAUNCH("attention", qa::attention<T>(s, qkv, d_cu, n_win, d.n_heads, D, att));
+        QA_LAUNCH("attention", qa::attention<T>(s, qkv, d_cu, n_win, d.n_heads, D, max_seg, att));
         QA_LAUNCH("o_proj", qa::gemm_bias_resid<T>(s, att, n_tok, D, e->W<T>(lw.o_w), D, e->W<float>(lw.o_b), x));
         QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b), h));
         QA_LAUNCH("fc1", qa::gemm_bias<T>(s, h, n_tok, D, e->W<T>(lw.fc1_w), F, e->W<float>(lw.fc1_b), u, true));
@@ -687,6 +691,11 @@ QA_API int qa_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, in
         if (!valid_len(lengths[i])) {
             set_err("clip %d has %lld samples: must be 0 or in 201..%lld", i, (long long)lengths[i],
                     (long long)kMaxSamples);
+            return QA_STATUS_INVALID_PARAMS;
+        }
+        if (e->d.window_chunks == 0 && lengths[i] > kMaxFullInput) {
+            set_err("clip %d has %lld samples: full-input attention takes clips of at most 30 s (%lld)", i,
+                    (long long)lengths[i], (long long)kMaxFullInput);
             return QA_STATUS_INVALID_PARAMS;
         }
         total += lengths[i];

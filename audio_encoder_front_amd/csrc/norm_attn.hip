@@ -1,5 +1,7 @@
 // LayerNorm (fp32 statistics, one wave per row) and block-diagonal windowed
-// multi-head attention (one workgroup per (window, head)).
+// multi-head attention (one workgroup per (window, head)), plus the
+// full-input variant with one attention segment per clip (OneSpeech "Front
+// end and graph numerics": CPU graphs attend over the whole bounded input).
 //
 // qwenasr.cpp ARCHITECTURE.md "Windowed audio tower": pre-norm blocks with
 // LayerNorm carrying a bias; bidirectional attention without RoPE, scaled by
@@ -263,17 +265,153 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     }
 }
 
+// Segments longer than 128 tokens (full-input attention over a whole clip):
+// one workgroup per (segment, head, group of 64 queries), one 16-query tile
+// per wave; keys stream through LDS in blocks of 128 with an online softmax
+// (running max and sum per query, the partial output rescaled when the max
+// grows).  Same MFMA layouts as the windowed kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void attention_long_kernel(const T* __restrict__ qkv, const int* __restrict__ cu,
+                                                             int n_heads, int d, int qgroups, T* __restrict__ out) {
+    constexpr int QR = AttnLds<T>::qrow, VR = AttnLds<T>::vrow;
+    constexpr int PER = Elem<T>::per16;
+    constexpr int CPR = kHd / PER;
+    constexpr int KBN = kHd * (int)sizeof(T) / 64;
+    constexpr int NCH = kMaxWindow * CPR / 256;
+    __shared__ __align__(16) char ks[kMaxWindow * QR];
+    __shared__ __align__(16) char vts[kHd * VR];
+
+    const int qg = blockIdx.x % qgroups;
+    const int sh = blockIdx.x / qgroups;
+    const int seg = sh / n_heads, h = sh % n_heads;
+    const int s0 = cu[seg], n = cu[seg + 1] - s0;
+    if (qg * 64 >= n) return;                       // whole workgroup idle (uniform)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int fr = lane & 15, fg = lane >> 4;
+    const size_t ld = 3 * (size_t)d;
+    const int qt = qg * 4 + wave;
+    const bool active = qt * 16 < n;                // wave-uniform
+    uint4 qf[KBN];
+    {
+        const int q = qt * 16 + fr;
+        const T* row = qkv + (size_t)(s0 + q) * ld + h * kHd + fg * PER;
+#pragma unroll
+        for (int kb = 0; kb < KBN; ++kb) qf[kb] = q < n ? ld16(row + kb * (64 / (int)sizeof(T))) : zero16();
+    }
+    const float sc = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < n; k0 += kMaxWindow) {
+        __syncthreads();                            // previous key block consumed
+        uint4 kv[NCH], vv[NCH];
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            const int idx = tid + q * 256;
+            const int t = idx / CPR, c = idx % CPR;
+            kv[q] = vv[q] = zero16();
+            if (k0 + t < n) {
+                const T* row = qkv + (size_t)(s0 + k0 + t) * ld + d + h * kHd + c * PER;
+                kv[q] = ld16(row);
+                vv[q] = ld16(row + d);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            const int idx = tid + q * 256;
+            const int t = idx / CPR, c = idx % CPR;
+            st16(ks + t * QR + c * 16, kv[q]);
+            const T* ve = reinterpret_cast<const T*>(&vv[q]);
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                *reinterpret_cast<T*>(vts + (c * PER + e) * VR + t * sizeof(T)) = ve[e];
+        }
+        __syncthreads();
+        if (!active) continue;
+        f32x4 sacc[8];
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KBN; ++kb) {
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                const uint4 kf = ld16(ks + (kt * 16 + fr) * QR + fg * 16 + kb * 64);
+                mfma_kblock(T(), kf, qf[kb], sacc[kt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = k0 + kt * 16 + 4 * fg + r;
+                const float v = key < n ? sacc[kt][r] * sc : -INFINITY;
+                sacc[kt][r] = v;
+                bm = fmaxf(bm, v);
+            }
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m, bm);
+        const float alpha = exp2f(m - mn);          // 0 on the first block
+        float bs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2f(sacc[kt][r] - mn);
+                sacc[kt][r] = p;
+                bs += p;
+            }
+        bs += __shfl_xor(bs, 16);
+        bs += __shfl_xor(bs, 32);
+        l = l * alpha + bs;
+        m = mn;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] = o[dt] * alpha;
+        if (sizeof(T) == 2) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                pv_step(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                pv_step(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    const int q = qt * 16 + fr;
+    if (active && q < n) {
+        const float inv = 1.0f / l;
+        T* orow = out + (size_t)(s0 + q) * d + h * kHd;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            store4(orow + dt * 16 + 4 * fg, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    }
+}
+
 template <typename T>
 hipError_t attention(hipStream_t s, const T* qkv, const int* cu_seqlens, int n_windows, int n_heads,
-                     int d, T* out) {
+                     int d, int max_len, T* out) {
     if (n_windows <= 0) return hipSuccess;
-    attention_kernel<T><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);
+    if (max_len <= kMaxWindow) {
+        attention_kernel<T><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);
+    } else {
+        const int qgroups = (max_len + 63) / 64;
+        attention_long_kernel<T><<<n_windows * n_heads * qgroups, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d,
+                                                                             qgroups, out);
+    }
     return hipGetLastError();
 }
 
 template hipError_t layernorm<float>(hipStream_t, const float*, int, int, const float*, const float*, float*);
 template hipError_t layernorm<bf16>(hipStream_t, const float*, int, int, const float*, const float*, bf16*);
-template hipError_t attention<float>(hipStream_t, const float*, const int*, int, int, int, float*);
-template hipError_t attention<bf16>(hipStream_t, const bf16*, const int*, int, int, int, bf16*);
+template hipError_t attention<float>(hipStream_t, const float*, const int*, int, int, int, int, float*);
+template hipError_t attention<bf16>(hipStream_t, const bf16*, const int*, int, int, int, int, bf16*);
 
 }  // namespace qa

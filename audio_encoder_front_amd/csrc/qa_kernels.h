@@ -77,8 +77,10 @@ hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, in
 // ---- LayerNorm (fp32 in, T out) and windowed attention
 template <typename T>
 hipError_t layernorm(hipStream_t s, const float* x, int M, int d, const float* g, const float* b, T* out);
+// Attention over independent segments [cu[i], cu[i+1]) of at most max_len
+// tokens (any length; segments over 128 tokens take the online-softmax path).
 template <typename T>
 hipError_t attention(hipStream_t s, const T* qkv, const int* cu_seqlens, int n_windows, int n_heads,
-                     int d, T* out);
+                     int d, int max_len, T* out);
 
 }  // namespace qa

@@ -11,7 +11,8 @@
  *          flatten channel-outer / frequency-inner, conv_out Linear (no bias),
  *          plus a sinusoidal position table that restarts at every chunk
  *       -> n_layers pre-LN transformer blocks whose bidirectional attention is
- *          confined to windows of 13 * window_chunks tokens of each clip
+ *          confined to windows of 13 * window_chunks tokens of each clip (or,
+ *          with window_chunks = 0, spans each whole clip of at most 30 s)
  *       -> post LayerNorm, proj1 (d -> d), GELU, proj2 (d -> output_dim).
  *
  * Sources (pages on Qwen3-ASR):
@@ -68,7 +69,10 @@ typedef struct qa_dims {
     int ffn_dim;          /* encoder_ffn_dim, multiple of 64 */
     int output_dim;       /* output_dim, multiple of 64 */
     int chunk_frames;     /* n_window * 2: must be 100 */
-    int window_chunks;    /* n_window_infer / chunk_frames: 1..8 (8 -> 104-token windows) */
+    int window_chunks;    /* n_window_infer / chunk_frames: 1..8 (8 -> 104-token windows), or 0 for
+                             full-input attention: one segment per clip, clips of at most 30 s
+                             (OneSpeech "Front end and graph numerics": the CPU graphs attend over
+                             the whole bounded input; longer audio is chunked before encoding) */
     int dtype;            /* QA_DTYPE_F32 or QA_DTYPE_BF16 */
 } qa_dims;
 
@@ -122,7 +126,8 @@ int qa_encoder_set_stream(qa_encoder *e, void *hip_stream);
  *   pcm      DEVICE pointer, float32, all clips concatenated in `lengths`
  *            order (sum(lengths) samples, 16 kHz mono).  Caller-owned.
  *   lengths  HOST array of n_clips int64 sample counts.  0 = empty clip (no
- *            tokens); otherwise 201 .. 19,200,000.
+ *            tokens); otherwise 201 .. 19,200,000 (201 .. 480,000 with
+ *            full-input attention, dims.window_chunks = 0).
  *   n_clips  >= 0.
  *   out      DEVICE pointer, float32 [sum_i qa_encode_num_tokens(lengths[i])
  *            x output_dim], rows clip-major, then chunk, then token-in-chunk.

@@ -19,6 +19,7 @@ N_MELS = 128
 F_MAX = 8000.0
 LN_EPS = 1e-5            # not stated on the pages; PyTorch LayerNorm default
 MAX_SAMPLES = 20 * 60 * SAMPLE_RATE   # [M*]: a request hears up to 20 minutes
+MAX_FULL_INPUT = 30 * SAMPLE_RATE     # [OneSpeech]: longer inputs are chunked before recognition
 
 
 class InvalidInput(ValueError):
@@ -322,12 +323,18 @@ def encode_clip(x: np.ndarray, W: Dict[str, np.ndarray], n_layers: int, n_heads:
                 taps: Optional[dict] = None) -> Dict[int, np.ndarray]:
     """Forward of one clip.  Returns {window index: output rows [w, out]}.
 
+    window_chunks = 0 selects full-input attention: the whole clip (at most
+    30 s) is one attention segment ([OneSpeech] "Front end and graph
+    numerics": the CPU graphs attend over the whole bounded input).
+
     The front end runs over the whole clip (its max normalises every frame);
     after it, chunks never mix and attention never crosses a window, so a
     window's rows depend only on its own 8 chunks.  `windows` selects which
     windows to compute (all if None) -- the definition restricted to them.
     """
     validate_clip(x.shape[0])
+    if window_chunks == 0 and x.shape[0] > MAX_FULL_INPUT:
+        raise InvalidInput("full-input attention takes clips of at most 30 s")
     if x.shape[0] == 0:
         return {}
     mel = log_mel(x)
@@ -337,12 +344,14 @@ def encode_clip(x: np.ndarray, W: Dict[str, np.ndarray], n_layers: int, n_heads:
     offs = np.concatenate([[0], np.cumsum(lens)])
     per_chunk = [after_cnn_len(m) for m in lens]
     n_tok = sum(per_chunk)
-    win_tok = after_cnn_len(chunk) * window_chunks
-    wb = window_bounds(n_tok, win_tok)
+    if window_chunks == 0:            # full-input attention: one segment per clip
+        wb, per_win = [(0, n_tok)], len(lens)
+    else:
+        wb, per_win = window_bounds(n_tok, after_cnn_len(chunk) * window_chunks), window_chunks
     sel = range(len(wb)) if windows is None else windows
     out = {}
     for wi in sel:
-        c0, c1 = wi * window_chunks, min((wi + 1) * window_chunks, len(lens))
+        c0, c1 = wi * per_win, min((wi + 1) * per_win, len(lens))
         rows, pre_pe = [], []
         for c in range(c0, c1):
             t = stem_chunk(mel[:, offs[c]:offs[c + 1]], W, lens[c], tail)

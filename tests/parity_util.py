@@ -64,13 +64,13 @@ def compare(dims, weights, clips, gpu_out, gpu_taps, windows_per_clip=None, chec
     tok_off = 0
     frame_off = 0
     worst = {"log_mel": 0.0, "window": 0.0, "stem": 0.0, "layer0": 0.0, "windows_checked": 0}
-    win_tok = 13 * dims.window_chunks
     for ci, x in enumerate(clips):
         n = len(x)
         nt = O.clip_num_tokens(n)
         nf = n // 160
         if n == 0:
             continue
+        win_tok = 13 * dims.window_chunks if dims.window_chunks else nt   # 0: one segment per clip
         nw = len(O.window_bounds(nt, win_tok))
         sel = None if windows_per_clip is None else sorted(set(windows_per_clip(ci, nw)))
         taps = {}

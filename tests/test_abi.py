@@ -70,7 +70,7 @@ def _tiny_weights():
 
 
 @pytest.mark.parametrize("field,value", [("n_mels", 80), ("head_dim", 32), ("chunk_frames", 50),
-                                         ("window_chunks", 0), ("window_chunks", 10), ("conv_channels", 48),
+                                         ("window_chunks", -1), ("window_chunks", 10), ("conv_channels", 48),
                                          ("d_model", 200), ("n_heads", 3), ("ffn_dim", 1000),
                                          ("output_dim", 250), ("n_layers", -1), ("dtype", 5)])
 def test_create_rejects_bad_dims(qa, field, value):

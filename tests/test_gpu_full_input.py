@@ -1,0 +1,61 @@
+"""GPU parity of the full-input attention variant (window_chunks = 0: one
+attention segment per clip of at most 30 s) against the oracle, for the fp32
+tiny encoder and the 0.6B-shaped bf16 encoder; segments of up to 128 tokens
+take the single-block kernel, longer ones the online-softmax kernel."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from parity_util import compare, make_encoder, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny_full():
+    dims = dataclasses.replace(synth.DIMS_TINY, window_chunks=0)
+    w = synth.make_weights(dims, 100)
+    enc = make_encoder(dims, w)
+    yield dims, w, enc
+    enc.free()
+
+
+def test_tiny_full_input_ragged_batch(tiny_full):
+    dims, w, enc = tiny_full
+    # 26, 0, 117 (9 full chunks, one block), 137 and 390 tokens (several key
+    # blocks, ragged last block), 1 token
+    lens = [32000, 0, 900 * 160, 16000 * 10 + 8000, 480000, 201]
+    clips = [synth.speech_like_clip(n, [90, i]) for i, n in enumerate(lens)]
+    print("case: tiny encoder, full-input attention", lens, flush=True)
+    out, taps = run_gpu(enc, clips, taps=True)
+    assert out.shape[0] == sum(O.clip_num_tokens(n) for n in lens)
+    rep = compare(dims, w, clips, out, taps)
+    print("tiny full-input", rep, flush=True)
+
+
+def test_full_input_rejects_clips_over_30s(tiny_full):
+    import torch
+    import audio_encoder_front_amd as qa
+    dims, w, enc = tiny_full
+    n = 480001
+    pcm = torch.zeros(n, device="cuda")
+    out = torch.empty((qa.qa_encode_num_tokens(n), dims.output_dim), device="cuda")
+    with pytest.raises(qa.QAError) as ei:
+        qa.qa_encode(enc, pcm, [n], out)
+    assert ei.value.status == qa._binding.QA_STATUS_INVALID_PARAMS
+
+
+def test_b06_full_input(tmp_path):
+    dims = dataclasses.replace(synth.DIMS_06B, window_chunks=0)
+    w = synth.make_weights(dims, 106)
+    enc = make_encoder(dims, w)
+    lens = [480000, 12 * 16000 + 77, 3 * 16000]
+    clips = [synth.speech_like_clip(n, [91, i]) for i, n in enumerate(lens)]
+    print("case: 0.6B bf16, full-input attention", lens, flush=True)
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(dims, w, clips, out, taps)
+    print("b06 full-input", rep, flush=True)
+    enc.free()

@@ -182,3 +182,23 @@ def test_packed_batch_is_clipwise():
     parts = [O.encode([x], W, 2, 2) for x in xs]
     assert np.array_equal(packed, np.concatenate(parts))
     assert packed.shape[0] == sum(O.clip_num_tokens(len(x)) for x in xs)
+
+
+def test_full_input_attention_reading():
+    # window_chunks = 0: one attention segment over the whole clip; equal to
+    # the windowed forward whenever the clip fits one window, different (and
+    # window-coupled) beyond it; clips over 30 s are refused.
+    dims, W = _small_weights()
+    short = synth.speech_like_clip(16000 * 5, [97, 0])          # 65 tokens < 104
+    a = O.encode_clip(short, W, 2, 2, window_chunks=0)
+    b = O.encode_clip(short, W, 2, 2, window_chunks=8)
+    assert np.allclose(a[0], b[0], atol=1e-12)
+    long = synth.speech_like_clip(16000 * 12, [97, 1])          # 156 tokens: 2 windows
+    full = O.encode_clip(long, W, 2, 2, window_chunks=0)[0]
+    win = O.encode_clip(long, W, 2, 2, window_chunks=8)
+    assert full.shape[0] == 156 and not np.allclose(full[:104], win[0])
+    x2 = long.copy(); x2[16000 * 11:] *= 0.5                    # touch only the last window's audio
+    full2 = O.encode_clip(x2, W, 2, 2, window_chunks=0)[0]
+    assert not np.allclose(full2[:52], full[:52])                # early rows see it under full attention
+    with pytest.raises(O.InvalidInput):
+        O.encode_clip(synth.speech_like_clip(30 * 16000 + 1, [97, 2]), W, 2, 2, window_chunks=0)
