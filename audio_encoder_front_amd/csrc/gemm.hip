@@ -155,6 +155,7 @@ struct EpiBias {           // out = acc + bias (optionally GELU), stored as T
     const float* bias;
     int M, N;
     bool gelu;
+    __device__ f32x4 init(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ void operator()(int m, int n, f32x4 v) const {
         if (m >= M || n >= N) return;
         const float4 b = *reinterpret_cast<const float4*>(bias + n);
@@ -164,17 +165,21 @@ struct EpiBias {           // out = acc + bias (optionally GELU), stored as T
     }
 };
 
-struct EpiResid {          // x += acc + bias (fp32 residual stream)
+struct EpiResid {          // x = x + bias + acc (fp32 residual stream)
     float* x;
     const float* bias;
     int M, N;
+    // The accumulators start from x + bias (read before the K loop, so the
+    // read overlaps the first stages instead of a read-modify-write at the end).
+    __device__ f32x4 init(int m, int n) const {
+        if (m >= M || n >= N) return f32x4{0.f, 0.f, 0.f, 0.f};
+        const float4 b = *reinterpret_cast<const float4*>(bias + n);
+        const float4 r = *reinterpret_cast<const float4*>(x + (size_t)m * N + n);
+        return f32x4{r.x + b.x, r.y + b.y, r.z + b.z, r.w + b.w};
+    }
     __device__ void operator()(int m, int n, f32x4 v) const {
         if (m >= M || n >= N) return;
-        const float4 b = *reinterpret_cast<const float4*>(bias + n);
-        float4* p = reinterpret_cast<float4*>(x + (size_t)m * N + n);
-        float4 r = *p;
-        r.x += v[0] + b.x; r.y += v[1] + b.y; r.z += v[2] + b.z; r.w += v[3] + b.w;
-        *p = r;
+        store4(x + (size_t)m * N + n, v[0], v[1], v[2], v[3]);
     }
 };
 
@@ -182,6 +187,7 @@ struct EpiF32Bias {        // out = acc + bias, fp32
     float* out;
     const float* bias;
     int M, N;
+    __device__ f32x4 init(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ void operator()(int m, int n, f32x4 v) const {
         if (m >= M || n >= N) return;
         const float4 b = *reinterpret_cast<const float4*>(bias + n);
@@ -195,6 +201,7 @@ struct EpiPE {             // x = acc + pe[src[m] % 13]; tap = acc
     const float* pe;
     const int* src;
     int M, N;
+    __device__ f32x4 init(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ void operator()(int m, int n, f32x4 v) const {
         if (m >= M || n >= N) return;
         const int j = src[m] % kChunkTok;
@@ -275,17 +282,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
         for (int q = 0; q < BI; ++q) dma16(wl.addr(wlane, q, kw), sb + q * 1024);
     };
 
+    const int nk = (K + KSTEP - 1) / KSTEP;
+    issue(0, 0);
+    const int fr = lane & 15, fg = lane >> 4;
     f32x4 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = ep.init(m0 + (wm * TM + i) * 16 + fr, n0 + (wn * TN + j) * 16 + 4 * fg);
 
-    const int nk = (K + KSTEP - 1) / KSTEP;
-    issue(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int fr = lane & 15, fg = lane >> 4;
     int sw[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sw[kb] = swz<BKB>(fr, kb * 4 + fg) * 16;
