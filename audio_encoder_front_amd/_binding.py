@@ -28,7 +28,8 @@ QA_TAP_LAYER0 = 2
 
 EXPORTS = ("qa_abi_version", "qa_last_error", "qa_encode_num_tokens", "qa_encoder_create",
            "qa_encoder_set_stream", "qa_encode", "qa_encoder_enable_taps", "qa_encoder_tap",
-           "qa_encoder_set_profiling", "qa_encoder_kernel_times", "qa_encoder_free")
+           "qa_encoder_set_profiling", "qa_encoder_kernel_times", "qa_encoder_set_profiling_label",
+           "qa_encoder_free")
 
 
 class qa_dims(C.Structure):
@@ -79,6 +80,8 @@ def _load() -> C.CDLL:
     lib.qa_encoder_tap.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int64]
     lib.qa_encoder_set_profiling.restype = C.c_int
     lib.qa_encoder_set_profiling.argtypes = [C.c_void_p, C.c_int]
+    lib.qa_encoder_set_profiling_label.restype = C.c_int
+    lib.qa_encoder_set_profiling_label.argtypes = [C.c_void_p, C.c_char_p]
     lib.qa_encoder_kernel_times.restype = C.c_int
     lib.qa_encoder_kernel_times.argtypes = [C.c_void_p, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
                                             C.POINTER(C.c_int64), C.c_int]
@@ -217,6 +220,11 @@ def qa_encoder_tap(enc: Encoder, tap: int, dst) -> int:
 
 def qa_encoder_set_profiling(enc: Encoder, enable: bool) -> None:
     _check(_lib.qa_encoder_set_profiling(enc.handle, 1 if enable else 0))
+
+
+def qa_encoder_set_profiling_label(enc: Encoder, label: Optional[str]) -> None:
+    """Time only the launches labelled `label` (None: every launch)."""
+    _check(_lib.qa_encoder_set_profiling_label(enc.handle, label.encode() if label else None))
 
 
 def qa_encoder_kernel_times(enc: Encoder) -> Dict[str, tuple]:

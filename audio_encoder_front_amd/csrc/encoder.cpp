@@ -181,6 +181,7 @@ struct qa_encoder {
     float *tap_logmel = nullptr, *tap_stem = nullptr, *tap_layer0 = nullptr;
     // profiling
     bool profiling = false;
+    std::string prof_only;                  // non-empty: time only launches with this label
     std::vector<hipEvent_t> ev_pool;
     std::vector<Profile> prof_cur;
     std::map<std::string, std::pair<double, int64_t>> prof_acc;
@@ -430,6 +431,12 @@ QA_API int qa_encoder_set_profiling(qa_encoder* e, int enable) {
     return QA_STATUS_OK;
 }
 
+QA_API int qa_encoder_set_profiling_label(qa_encoder* e, const char* label) {
+    if (!e) { set_err("encoder is NULL"); return QA_STATUS_INVALID_PARAMS; }
+    e->prof_only = label ? label : "";
+    return QA_STATUS_OK;
+}
+
 QA_API int qa_encoder_kernel_times(qa_encoder* e, const char** labels, double* total_ms, int64_t* launches,
                                    int cap) {
     if (!e || cap < 0 || (cap > 0 && (!labels || !total_ms || !launches))) {
@@ -599,7 +606,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     e->prof_cur.clear();
     size_t ev_next = 0;
     auto launch = [&](const char* label, auto&& fn) -> hipError_t {
-        if (!e->profiling) return fn();
+        if (!e->profiling || (!e->prof_only.empty() && e->prof_only != label)) return fn();
         while (e->ev_pool.size() < ev_next + 2) {
             hipEvent_t ev;
             hipError_t st = hipEventCreate(&ev);

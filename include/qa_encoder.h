@@ -159,6 +159,12 @@ int qa_encoder_set_profiling(qa_encoder *e, int enable);
 int qa_encoder_kernel_times(qa_encoder *e, const char **labels, double *total_ms,
                             int64_t *launches, int cap);
 
+/* Restrict the profiling events to the launches labelled `label` (a copy is
+ * kept; NULL or "" = every launch, the default), so that a timed run carries
+ * two events per such launch instead of two per kernel.  Returns
+ * QA_STATUS_OK or INVALID_PARAMS (NULL handle). */
+int qa_encoder_set_profiling_label(qa_encoder *e, const char *label);
+
 /* Release device memory and the handle.  NULL is a no-op. */
 void qa_encoder_free(qa_encoder *e);
 
