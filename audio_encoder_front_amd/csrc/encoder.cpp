@@ -19,6 +19,7 @@
 #include <map>
 #include <new>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/qa_encoder.h"
@@ -165,6 +166,7 @@ struct qa_encoder {
     int device = 0;
     // weights + constants in one device allocation
     char* wbuf = nullptr;
+    size_t conv1_frag = 0;              // bf16 MFMA fragments of conv1 (0: VALU kernel)
     size_t conv1_w = 0, conv1_b = 0, conv2_w = 0, conv2_b = 0, conv3_w = 0, conv3_b = 0, conv_out_w = 0;
     std::vector<LayerW> layers;
     size_t post_ln_w = 0, post_ln_b = 0, proj1_w = 0, proj1_b = 0, proj2_w = 0, proj2_b = 0;
@@ -336,6 +338,26 @@ QA_API qa_encoder* qa_encoder_create(const qa_weights* w, const qa_dims* d) {
             for (int k = 0; k < 9; ++k) r[(size_t)k * C + c] = v[(size_t)c * 9 + k];
         e->conv1_w = put_f32(r);
         e->conv1_b = put_f32(f32vec(w->conv1_b, C));
+        if (d->dtype == QA_DTYPE_BF16 && C <= qa::kConv1MfmaMaxC) {
+            // A operand of lane l for channel tile t: channel 32 (t / 2) + 8 (r / 4) +
+            // 4 (t % 2) + r % 4 with r = l % 16, K entries k = 8 (l / 16) + e: tap
+            // k / 3 for k < 27 (three copies, one per input part), the bias at
+            // k = 27, zero beyond.
+            const uint16_t* wb = static_cast<const uint16_t*>(w->conv1_w);
+            const uint16_t* bb = static_cast<const uint16_t*>(w->conv1_b);
+            std::vector<uint16_t> fr((size_t)(C / 16) * 64 * 8, 0);
+            for (int t = 0; t < C / 16; ++t)
+                for (int l = 0; l < 64; ++l)
+                    for (int el = 0; el < 8; ++el) {
+                        const int r = l % 16, k = 8 * (l / 16) + el;
+                        const int c = 32 * (t / 2) + 8 * (r / 4) + 4 * (t % 2) + r % 4;
+                        uint16_t v = 0;
+                        if (k < 27) v = wb[(size_t)c * 9 + k / 3];
+                        else if (k == 27) v = bb[c];
+                        fr[((size_t)t * 64 + l) * 8 + el] = v;
+                    }
+            e->conv1_frag = pk.put(fr.data(), fr.size() * 2);
+        }
     }
     // conv2/conv3 [Co][Ci][3][3] -> [Co][K], K index (ci / 32, tap, ci % 32)
     auto conv_pack = [&](const void* p) {
@@ -635,9 +657,17 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     QA_LAUNCH("frontend", qa::frontend(s, pcm, d_clips, d_tiles, n_tiles, e->W<float>(e->basis), e->W<float>(e->fbB),
                                        e->W<int>(e->fb_range), logmel, key, flag));
     QA_LAUNCH("normalize", qa::normalize(s, logmel, d_clips, d_tiles, n_tiles, key));
-    QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
-    QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1, n_chunks, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b), c2, false));
-    QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2, n_chunks, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b), c3, true));
+    if constexpr (std::is_same<T, qa::bf16>::value) {
+        if (e->conv1_frag)
+            QA_LAUNCH("conv1", qa::conv1_mfma(s, logmel, d_chunks, n_chunks, e->W<uint4>(e->conv1_frag), C, c1));
+        else
+            QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
+    } else {
+        QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
+    }
+    const bool c1_blocked = std::is_same<T, qa::bf16>::value && e->conv1_frag != 0;   // MFMA conv1 layout
+    QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1, n_chunks, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b), c2, false, c1_blocked));
+    QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2, n_chunks, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b), c3, true, false));
     QA_LAUNCH("conv_out", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), x, nullptr));
     if (e->taps)
         QA_LAUNCH("tap_stem", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), tl0, tstem));

@@ -103,10 +103,13 @@ struct GatherA {   // row m of the GEMM is row src[m] of a
 };
 
 template <typename T>
-struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv over NHWC input
+struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
     const T* in;
     int M, Hin, Win, C, Hout, Wout;
     bool time_major;                  // output row order (chunk, j, i) instead of (chunk, i, j)
+    // Input layout per chunk: NHWC [Hin][Win][C] (pstride = C, cbstride = 32) or
+    // channel-blocked [C / 32][Hin][Win][32] (pstride = 32, cbstride = Hin Win 32).
+    int pstride, cbstride;
     template <int AI, int RS>
     struct Lane { int chunk[AI]; int rc[AI]; };   // rc = (2i-1) << 16 | (2j-1) & 0xffff
     struct KCtx { int a, b, off; bool ok; };
@@ -133,7 +136,7 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv over NHWC inp
         const int cb = k0 / (9 * kConvCB), rem = k0 - cb * (9 * kConvCB);
         const int tap = rem / kConvCB, ci = cb * kConvCB + (rem - tap * kConvCB);
         const int a = tap / 3;
-        return KCtx{a, tap - 3 * a, ci * (int)sizeof(T), k0 < 9 * C};
+        return KCtx{a, tap - 3 * a, (cb * cbstride + (ci - cb * kConvCB)) * (int)sizeof(T), k0 < 9 * C};
     }
     template <int AI, int RS>
     __device__ const void* addr(const Lane<AI, RS>& l, int q, const KCtx& k) const {
@@ -141,7 +144,7 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv over NHWC inp
         const int col = (int)(short)(l.rc[q] & 0xffff) + k.b;
         if (l.chunk[q] < 0 || !k.ok || (unsigned)r >= (unsigned)Hin || (unsigned)col >= (unsigned)Win)
             return g_zero16;
-        return reinterpret_cast<const char*>(in + ((size_t)l.chunk[q] * Hin * Win + (size_t)r * Win + col) * C) +
+        return reinterpret_cast<const char*>(in + (size_t)l.chunk[q] * Hin * Win * C + (size_t)(r * Win + col) * pstride) +
                k.off;
     }
 };
@@ -384,10 +387,12 @@ static hipError_t run(hipStream_t s, const AL& al, int M, const T* w, int N, int
 
 template <typename T>
 hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win, int C,
-                     const T* w, const float* bias, T* out, bool time_major) {
+                     const T* w, const float* bias, T* out, bool time_major, bool blocked_in) {
     const int Hout = (Hin + 1) / 2, Wout = (Win + 1) / 2;
     const int M = n_chunks * Hout * Wout;
-    ConvA<T> al{in, M, Hin, Win, C, Hout, Wout, time_major};
+    if (C % kConvCB) return hipErrorInvalidValue;
+    ConvA<T> al{in, M, Hin, Win, C, Hout, Wout, time_major, blocked_in ? kConvCB : C,
+                blocked_in ? Hin * Win * kConvCB : kConvCB};
     EpiBias<T> ep{out, bias, M, C, true};
     if (C % Elem<T>::per16) return hipErrorInvalidValue;
     return time_major ? run<kConv3>(s, al, M, w, C, 9 * C, ep) : run<kConv2>(s, al, M, w, C, 9 * C, ep);
@@ -430,7 +435,7 @@ hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, in
 
 #define QA_INST(T)                                                                                    \
     template hipError_t conv3x3s2<T>(hipStream_t, const T*, int, int, int, int, const T*, const float*, \
-                                     T*, bool);                                                       \
+                                     T*, bool, bool);                                                 \
     template hipError_t conv_out<T>(hipStream_t, const T*, const int*, int, int, const T*, int,        \
                                     const float*, float*, float*);                                    \
     template hipError_t gemm_bias<T>(hipStream_t, const T*, int, int, const T*, int, const float*, T*, \

@@ -37,25 +37,24 @@ __device__ __forceinline__ void mfma_kblock(float, const uint4& a, const uint4& 
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
-// exp(-x^2) with t = 1 / (1 + p x); absolute error <= 1.5e-7; odd extension
-// for x < 0.  Branch-free: one reciprocal, one exp2, five FMAs.
-__device__ __forceinline__ float erf_as7126(float x) {
-    const float ax = fabsf(x);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-    float y = fmaf(1.061405429f, t, -1.453152027f);
-    y = fmaf(y, t, 1.421413741f);
-    y = fmaf(y, t, -0.284496736f);
-    y = fmaf(y, t, 0.254829592f);
-    y *= t;
-    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * ax * ax);   // exp(-x^2)
-    return copysignf(fmaf(-y, e, 1.0f), x);
-}
-
-// GELU with the erf (not tanh) form: x * (1 + erf(x / sqrt 2)) / 2.
-__device__ __forceinline__ float gelu_erf(float x) {
-    return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f));
+// GELU with the erf (not tanh) form, gelu(z) = z (1 + erf(z / sqrt 2)) / 2,
+// written as relu(z) - a erfc(a / sqrt 2) / 2 with a = min(|z|, 6), and
+// erfc(a / sqrt 2) / 2 = exp2(P(a)) for a degree-6 polynomial P fitted to
+// log2(erfc(a / sqrt 2)) - 1, weighted by the GELU error it causes
+// (gelu_coeffs.py in this package derives and checks the coefficients).
+// Horner in fp32, one exp2: absolute error <= 2.7e-7 over the fp32 range
+// (float32 emulation against the exact erf); past |z| = 6 the tail term is
+// below 1e-8.  +inf maps to +inf, -inf to -0.
+__device__ __forceinline__ float gelu_erf(float z) {
+    const float a = __builtin_amdgcn_fmed3f(fabsf(z), 0.0f, 6.0f);
+    float y = 3.454265243e-05f;
+    y = fmaf(y, a, -7.817276055e-04f);
+    y = fmaf(y, a, 8.121271618e-03f);
+    y = fmaf(y, a, -5.347414687e-02f);
+    y = fmaf(y, a, -4.587250352e-01f);
+    y = fmaf(y, a, -1.151216626e+00f);
+    y = fmaf(y, a, -9.999914765e-01f);
+    return fmaf(-a, __builtin_amdgcn_exp2f(y), fmaxf(z, 0.0f));
 }
 
 // Store 4 consecutive values (fp32 -> 16 bytes, bf16 -> 8 bytes, RNE).
