@@ -61,7 +61,7 @@ def kernel_work(d, lengths):
         "proj1": (2 * T * D * D, T * D * e + D * D * e + T * D * e, "bf16"),
         "proj2": (2 * T * D * O, T * D * e + O * D * e + T * O * 4, "bf16"),
         "ln": (0, T * D * 4 + T * D * e, "hbm"),
-        "conv1": (2 * ch * 64 * 50 * C * 9, fr * 128 * 4 + ch * 64 * 50 * C * e, "fp32"),
+        "conv1": (2 * ch * 64 * 50 * C * 9, fr * 128 * 4 + ch * 64 * 50 * C * e, "hbm"),
         "normalize": (0, 2 * fr * 128 * 4, "hbm"),
     }
     return work, (ch, T, fr, wins)
@@ -69,8 +69,9 @@ def kernel_work(d, lengths):
 
 # Source files whose kernels the HBM-traffic figure in profiles/ was taken on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "b17_20m_traffic.json")
-KERNEL_SOURCES = ["audio_encoder_front_amd/csrc/gemm.hip", "audio_encoder_front_amd/csrc/qa_device.h",
-                  "audio_encoder_front_amd/csrc/qa_kernels.h"]
+KERNEL_SOURCES = ["audio_encoder_front_amd/csrc/" + f for f in
+                  ("gemm.hip", "stem.hip", "frontend.hip", "norm_attn.hip", "encoder.cpp", "qa_device.h",
+                   "qa_kernels.h")]
 
 
 def sources_digest() -> str:
