@@ -19,6 +19,9 @@ It is written from four web pages on Qwen3-ASR:
 Every function below is the plain definition: explicit cos/sin DFT matrices
 (no FFT), im2col + matmul convolution, dense softmax per window, no fusion.
 
+`oracle.resample` is the resampler to 16 kHz that [qwenasr] "Module map" puts
+in front of the front end (Kaiser polyphase; its parameters are a reading).
+
 Pins (see tests/test_oracle_*.py): every function is checked against closed
 forms, invariants, brute force or an independent library routine, except the
 whole-forward composition, which is pinned only through its pinned parts plus
