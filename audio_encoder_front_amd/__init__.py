@@ -9,4 +9,5 @@ from ._binding import (Encoder, QAError, encode, library, make_dims, qa_abi_vers
                        qa_encode_num_tokens, qa_encoder_create, qa_encoder_enable_taps, qa_encoder_free,
                        qa_encoder_kernel_times, qa_encoder_set_profiling, qa_encoder_set_profiling_label,
                        qa_encoder_set_stream,
-                       qa_encoder_tap, qa_last_error)
+                       qa_encoder_tap, qa_last_error, Resampler, qa_resample_length, qa_resampler_create,
+                       qa_resample, resample)

@@ -29,7 +29,7 @@ QA_TAP_LAYER0 = 2
 EXPORTS = ("qa_abi_version", "qa_last_error", "qa_encode_num_tokens", "qa_encoder_create",
            "qa_encoder_set_stream", "qa_encode", "qa_encoder_enable_taps", "qa_encoder_tap",
            "qa_encoder_set_profiling", "qa_encoder_kernel_times", "qa_encoder_set_profiling_label",
-           "qa_encoder_free")
+           "qa_encoder_free", "qa_resample_length", "qa_resampler_create", "qa_resample", "qa_resampler_free")
 
 
 class qa_dims(C.Structure):
@@ -87,6 +87,14 @@ def _load() -> C.CDLL:
                                             C.POINTER(C.c_int64), C.c_int]
     lib.qa_encoder_free.restype = None
     lib.qa_encoder_free.argtypes = [C.c_void_p]
+    lib.qa_resample_length.restype = C.c_int64
+    lib.qa_resample_length.argtypes = [C.c_int64, C.c_int]
+    lib.qa_resampler_create.restype = C.c_void_p
+    lib.qa_resampler_create.argtypes = [C.c_int]
+    lib.qa_resample.restype = C.c_int
+    lib.qa_resample.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
+    lib.qa_resampler_free.restype = None
+    lib.qa_resampler_free.argtypes = [C.c_void_p]
     return lib
 
 
@@ -248,4 +256,60 @@ def encode(enc: Encoder, pcm, lengths: Sequence[int], out=None):
     if out is None:
         out = torch.empty((total, enc.dims.output_dim), dtype=torch.float32, device=pcm.device)
     qa_encode(enc, pcm, lengths, out)
+    return out
+
+
+# ------------------------------------------------------------------ resampler
+
+class Resampler:
+    """Owns a qa_resampler handle (the filter table for one input rate)."""
+
+    def __init__(self, handle: int, rate: int):
+        self.handle = handle
+        self.rate = rate
+
+    def __del__(self):
+        self.free()
+
+    def free(self):
+        if getattr(self, "handle", None):
+            _lib.qa_resampler_free(self.handle)
+            self.handle = None
+
+
+def qa_resample_length(n_in: int, rate_in: int) -> int:
+    return _lib.qa_resample_length(int(n_in), int(rate_in))
+
+
+def qa_resampler_create(rate_in: int) -> Resampler:
+    h = _lib.qa_resampler_create(int(rate_in))
+    if not h:
+        raise QAError(QA_STATUS_INVALID_PARAMS, qa_last_error())
+    return Resampler(h, int(rate_in))
+
+
+def qa_resample(r: Resampler, stream, pcm_in, out) -> None:
+    """pcm_in, out: contiguous float32 CUDA tensors; out must hold
+    qa_resample_length(len(pcm_in), r.rate) samples."""
+    import torch
+    n = int(pcm_in.numel())
+    need = qa_resample_length(n, r.rate)
+    if pcm_in.dtype != torch.float32 or out.dtype != torch.float32 or not pcm_in.is_cuda or not out.is_cuda:
+        raise QAError(QA_STATUS_INVALID_PARAMS, "pcm_in and out must be float32 device tensors")
+    if not pcm_in.is_contiguous() or not out.is_contiguous() or out.numel() < need:
+        raise QAError(QA_STATUS_INVALID_PARAMS, f"out must be contiguous with at least {need} samples")
+    s = stream.cuda_stream if stream is not None and hasattr(stream, "cuda_stream") else (stream or 0)
+    _check(_lib.qa_resample(r.handle, C.c_void_p(s), C.c_void_p(pcm_in.data_ptr()), n,
+                            C.c_void_p(out.data_ptr())))
+
+
+def resample(r: Resampler, pcm_in, stream=None):
+    """Allocate the output on pcm_in's device and resample (asynchronous on `stream`,
+    default: torch's current stream)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(pcm_in.device)
+    out = torch.empty(max(qa_resample_length(int(pcm_in.numel()), r.rate), 0), dtype=torch.float32,
+                      device=pcm_in.device)
+    qa_resample(r, stream, pcm_in, out)
     return out

@@ -42,6 +42,14 @@ void set_err(const char* fmt, ...) {
     g_err = buf;
 }
 
+}  // namespace
+
+namespace qa {
+void set_error_message(const char* msg) { g_err = msg; }
+}  // namespace qa
+
+namespace {
+
 constexpr int64_t kMaxSamples = 20LL * 60 * 16000;   // a request hears up to 20 minutes
 constexpr int64_t kMaxFullInput = 30LL * 16000;      // bounded input of full-input attention (30 s)
 constexpr int kHop = 160;

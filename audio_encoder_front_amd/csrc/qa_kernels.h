@@ -39,6 +39,9 @@ constexpr int kChunkTok = 13;        // tokens per full chunk
 constexpr int kMaxWindow = 128;      // attention kernel capacity (tokens per window)
 constexpr int kConvCB = 32;          // input-channel block of the conv2/conv3 K order
 
+// Sets the thread-local message returned by qa_last_error.
+void set_error_message(const char* msg);
+
 // ---- front end
 hipError_t init_flags(hipStream_t s, int* clip_key, int n_clips, int* flag);
 hipError_t frontend(hipStream_t s, const float* pcm, const ClipInfo* clips, const FrontTile* tiles,

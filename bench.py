@@ -106,6 +106,34 @@ def copy_calibration(nbytes: int = 1 << 30):
     torch.cuda.synchronize()
 
 
+def resample_bench(dev, rate: int = 44100, seconds: int = 1200, reps: int = 10):
+    """The resampler in front of the front end, timed on its own: one
+    20-minute clip at 44.1 kHz to 16 kHz (not part of `value`)."""
+    import numpy as np
+    import torch
+    import audio_encoder_front_amd as qa
+    n = seconds * rate
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy((0.1 * rng.standard_normal(n)).astype(np.float32)).to(dev)
+    r = qa.qa_resampler_create(rate)
+    out = torch.empty(qa.qa_resample_length(n, rate), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        qa.qa_resample(r, stream, x, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        qa.qa_resample(r, stream, x, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    r.free()
+    nbytes = 4 * (n + out.numel())
+    return {"workload": f"one {seconds} s clip at {rate} Hz -> 16 kHz", "avg_ms": round(ms, 4),
+            "audio_s_per_s": round(seconds / (ms * 1e-3), 1), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "bound": "hbm", "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+
+
 def cpu_baseline(wl, seconds: float):
     """The fp64 oracle on the first `seconds` of the workload's first clip."""
     import numpy as np
@@ -236,6 +264,7 @@ def main():
         "kernels_note": f"per-kernel table from {prof_steps} separate steps with events around every launch; "
                         "the timed steps carry events only around the dominant kernel",
     }
+    res["resample"] = resample_bench(dev)
     if args.calibrate_copy:
         copy_calibration()
     if not args.no_cpu_baseline:

@@ -168,6 +168,38 @@ int qa_encoder_set_profiling_label(qa_encoder *e, const char *label);
 /* Release device memory and the handle.  NULL is a no-op. */
 void qa_encoder_free(qa_encoder *e);
 
+/* ------------------------------------------------------------------------
+ * Resampling to 16 kHz, the step in front of the front end (qwenasr.cpp
+ * ARCHITECTURE.md "Upstream model": any input is resampled to 16 kHz mono
+ * before the frontend; "Module map": a Kaiser polyphase resampler).  The page
+ * does not give the filter; this library's reading:
+ *   up / down = 16000 / rate_in reduced by their gcd; a linear-phase low-pass
+ *   FIR of 2 half + 1 taps, half = 10 max(up, down), cut-off 1 / max(up, down)
+ *   of the upsampled Nyquist frequency, Kaiser window beta = 5, unit DC gain,
+ *   scaled by up; output sample n is the filtered zero-stuffed input at
+ *   upsampled index n down (no delay), zeros outside the clip.  (The same
+ *   filter as scipy.signal.resample_poly(x, up, down, window=("kaiser", 5)).)
+ */
+typedef struct qa_resampler qa_resampler;   /* opaque: the filter table on the device */
+
+/* Output length for n_in samples at rate_in Hz: ceil(n_in up / down).
+ * -1 (qa_last_error set) if n_in < 0 or rate_in is outside 1000..768000. */
+int64_t qa_resample_length(int64_t n_in, int rate_in);
+
+/* Design the filter for rate_in (1000..768000 Hz) and copy its polyphase
+ * table to the current HIP device.  NULL on failure (qa_last_error says why). */
+qa_resampler *qa_resampler_create(int rate_in);
+
+/* Resample one mono clip: in = DEVICE float32 [n_in], out = DEVICE float32
+ * [qa_resample_length(n_in, rate_in)], both caller-owned, not overlapping.
+ * Enqueued on hip_stream (a hipStream_t; NULL = null stream), no
+ * synchronisation.  Returns QA_STATUS_OK, INVALID_PARAMS (NULL handle or
+ * pointers, n_in < 0) or ENCODE_FAILED (launch error). */
+int qa_resample(qa_resampler *r, void *hip_stream, const float *in, int64_t n_in, float *out);
+
+/* Release the table and the handle.  NULL is a no-op. */
+void qa_resampler_free(qa_resampler *r);
+
 #ifdef __cplusplus
 }
 #endif

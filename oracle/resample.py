@@ -86,19 +86,21 @@ def output_length(n: int, rate: int) -> int:
     return -(-n * up // down)
 
 
-def resample(x: np.ndarray, rate: int) -> np.ndarray:
+def resample(x: np.ndarray, rate: int, outputs=None) -> np.ndarray:
     """y[n] = sum_k h[k] u[n down + half - k], u the input zero-stuffed by up
     (u[i up] = x[i], zero elsewhere); only the terms with i = (n down + half -
-    k) / up an integer in [0, len(x)) contribute."""
+    k) / up an integer in [0, len(x)) contribute.  `outputs`: evaluate only
+    these output indices (default: all)."""
     x = np.asarray(x, dtype=np.float64)
     up, down, half, h = design(rate)
     n_out = output_length(x.shape[0], rate)
-    y = np.zeros(n_out)
-    for n in range(n_out):
+    ns = range(n_out) if outputs is None else list(outputs)
+    y = np.zeros(len(ns))
+    for o, n in enumerate(ns):
         t = n * down + half                 # upsampled index seen by tap k = 0
         k0 = t % up                          # first tap landing on an input sample
         ks = np.arange(k0, h.shape[0], up)
         idx = (t - ks) // up
         ok = (idx >= 0) & (idx < x.shape[0])
-        y[n] = np.dot(h[ks[ok]], x[idx[ok]])
+        y[o] = np.dot(h[ks[ok]], x[idx[ok]])
     return y

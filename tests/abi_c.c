@@ -68,6 +68,17 @@ int main(void) {
     CHECK(qa_encoder_kernel_times(NULL, labels, ms, cnt, 4) == -1);
     qa_encoder_free(NULL);
 
+    /* resampler: argument checks only (no device work) */
+    CHECK(qa_resample_length(44100, 44100) == 16000);
+    CHECK(qa_resample_length(3000, 44100) == 1089);
+    CHECK(qa_resample_length(0, 8000) == 0);
+    CHECK(qa_resample_length(-1, 44100) == -1);
+    CHECK(qa_resample_length(100, 999) == -1);
+    CHECK(qa_resampler_create(999) == NULL);
+    CHECK(qa_resampler_create(768001) == NULL);
+    CHECK(qa_resample(NULL, NULL, NULL, 10, NULL) == QA_STATUS_INVALID_PARAMS);
+    qa_resampler_free(NULL);
+
     if (fails) return 1;
     printf("abi_c: all checks passed\n");
     return 0;

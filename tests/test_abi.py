@@ -115,3 +115,15 @@ def test_strict_c99_consumer(tmp_path, qa):
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr + r.stdout
+
+
+def test_resample_length_matches_oracle(qa):
+    import oracle.resample as R
+    rng = np.random.default_rng(21)
+    for rate in (44100, 48000, 8000, 22050, 11025, 96000, 16000, 44056, 1000, 768000):
+        for n in [0, 1, 2, 441, 44100] + list(rng.integers(1, 60_000_000, 20)):
+            assert qa.qa_resample_length(int(n), rate) == R.output_length(int(n), rate), (rate, n)
+    assert qa.qa_resample_length(-1, 44100) == -1
+    assert qa.qa_resample_length(10, 999) == -1
+    with pytest.raises(qa.QAError):
+        qa.qa_resampler_create(768001)
