@@ -21,6 +21,9 @@ Every function below is the plain definition: explicit cos/sin DFT matrices
 
 `oracle.resample` is the resampler to 16 kHz that [qwenasr] "Module map" puts
 in front of the front end (Kaiser polyphase; its parameters are a reading).
+`oracle.thinker` is the step after the encoder: the audio splice into the
+prompt embeddings and the Qwen3 Thinker prefill ([qwenasr] "Qwen3 Thinker
+decoder", "Prompt assembly and audio splice").
 
 Pins (see tests/test_oracle_*.py): every function is checked against closed
 forms, invariants, brute force or an independent library routine, except the
