@@ -10,4 +10,5 @@ from ._binding import (Encoder, QAError, encode, library, make_dims, qa_abi_vers
                        qa_encoder_kernel_times, qa_encoder_set_profiling, qa_encoder_set_profiling_label,
                        qa_encoder_set_stream,
                        qa_encoder_tap, qa_last_error, Resampler, qa_resample_length, qa_resampler_create,
-                       qa_resample, resample)
+                       qa_resample, resample, Thinker, make_thinker_dims, qa_thinker_create,
+                       qa_thinker_set_stream, qa_thinker_prefill, thinker_prefill)

@@ -29,7 +29,8 @@ QA_TAP_LAYER0 = 2
 EXPORTS = ("qa_abi_version", "qa_last_error", "qa_encode_num_tokens", "qa_encoder_create",
            "qa_encoder_set_stream", "qa_encode", "qa_encoder_enable_taps", "qa_encoder_tap",
            "qa_encoder_set_profiling", "qa_encoder_kernel_times", "qa_encoder_set_profiling_label",
-           "qa_encoder_free", "qa_resample_length", "qa_resampler_create", "qa_resample", "qa_resampler_free")
+           "qa_encoder_free", "qa_resample_length", "qa_resampler_create", "qa_resample", "qa_resampler_free",
+           "qa_thinker_create", "qa_thinker_set_stream", "qa_thinker_prefill", "qa_thinker_free")
 
 
 class qa_dims(C.Structure):
@@ -48,6 +49,19 @@ class qa_weights(C.Structure):
                 + [(n, _VPP) for n in ("ln1_w", "ln1_b", "q_w", "q_b", "k_w", "k_b", "v_w", "v_b",
                                        "o_w", "o_b", "ln2_w", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
                 + [(n, _VP) for n in ("post_ln_w", "post_ln_b", "proj1_w", "proj1_b", "proj2_w", "proj2_b")])
+
+
+class qa_thinker_dims(C.Structure):
+    _fields_ = [(n, C.c_int) for n in ("abi_version", "hidden", "n_layers", "n_q_heads", "n_kv_heads", "head_dim",
+                                       "ffn_dim", "vocab", "dtype")]
+
+
+THINKER_LAYER_FIELDS = ("attn_norm", "q_w", "k_w", "v_w", "q_norm", "k_norm", "o_w", "ffn_norm", "gate_w", "up_w",
+                        "down_w")
+
+
+class qa_thinker_weights(C.Structure):
+    _fields_ = [("embed", _VP)] + [(n, _VPP) for n in THINKER_LAYER_FIELDS] + [("out_norm", _VP)]
 
 
 class QAError(RuntimeError):
@@ -87,6 +101,15 @@ def _load() -> C.CDLL:
                                             C.POINTER(C.c_int64), C.c_int]
     lib.qa_encoder_free.restype = None
     lib.qa_encoder_free.argtypes = [C.c_void_p]
+    lib.qa_thinker_create.restype = C.c_void_p
+    lib.qa_thinker_create.argtypes = [C.POINTER(qa_thinker_weights), C.POINTER(qa_thinker_dims)]
+    lib.qa_thinker_set_stream.restype = C.c_int
+    lib.qa_thinker_set_stream.argtypes = [C.c_void_p, C.c_void_p]
+    lib.qa_thinker_prefill.restype = C.c_int
+    lib.qa_thinker_prefill.argtypes = [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int64), C.c_int, C.c_void_p,
+                                       C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.c_void_p, C.c_void_p]
+    lib.qa_thinker_free.restype = None
+    lib.qa_thinker_free.argtypes = [C.c_void_p]
     lib.qa_resample_length.restype = C.c_int64
     lib.qa_resample_length.argtypes = [C.c_int64, C.c_int]
     lib.qa_resampler_create.restype = C.c_void_p
@@ -313,3 +336,101 @@ def resample(r: Resampler, pcm_in, stream=None):
                       device=pcm_in.device)
     qa_resample(r, stream, pcm_in, out)
     return out
+
+
+
+# ------------------------------------------------------------------ Thinker prefill
+
+class Thinker:
+    """Owns a qa_thinker handle."""
+
+    def __init__(self, handle: int, dims: qa_thinker_dims):
+        self.handle = handle
+        self.dims = dims
+
+    def __del__(self):
+        self.free()
+
+    def free(self):
+        if getattr(self, "handle", None):
+            _lib.qa_thinker_free(self.handle)
+            self.handle = None
+
+
+def make_thinker_dims(d) -> qa_thinker_dims:
+    """qa_thinker_dims from any object/mapping with the ThinkerDims fields."""
+    get = (lambda k: d[k]) if isinstance(d, Mapping) else (lambda k: getattr(d, k))
+    dt = get("dtype")
+    dt = {"f32": QA_DTYPE_F32, "bf16": QA_DTYPE_BF16}.get(dt, dt)
+    return qa_thinker_dims(QA_ABI_VERSION, get("hidden"), get("n_layers"), get("n_q_heads"), get("n_kv_heads"),
+                           get("head_dim"), get("ffn_dim"), get("vocab"), int(dt))
+
+
+def qa_thinker_create(weights: Dict[str, np.ndarray], dims) -> Thinker:
+    """weights: 'embed', 'out_norm' and 'layers.<l>.<field>' arrays in PyTorch layout."""
+    qd = make_thinker_dims(dims)
+    keep = []
+
+    def ptr(name):
+        b = _host_buffer(weights[name], qd.dtype)
+        keep.append(b)
+        return b.ctypes.data_as(C.c_void_p)
+
+    w = qa_thinker_weights()
+    w.embed = ptr("embed")
+    w.out_norm = ptr("out_norm")
+    L = qd.n_layers
+    for n in THINKER_LAYER_FIELDS:
+        arr = (C.c_void_p * max(L, 1))(*[ptr(f"layers.{l}.{n}") for l in range(L)])
+        keep.append(arr)
+        setattr(w, n, C.cast(arr, _VPP))
+    h = _lib.qa_thinker_create(C.byref(w), C.byref(qd))
+    if not h:
+        raise QAError(QA_STATUS_LOAD_FAILED, qa_last_error())
+    return Thinker(h, qd)
+
+
+def qa_thinker_set_stream(t: Thinker, stream) -> None:
+    raw = getattr(stream, "cuda_stream", stream)
+    _check(_lib.qa_thinker_set_stream(t.handle, C.c_void_p(raw or 0)))
+
+
+def qa_thinker_prefill(t: Thinker, prompts, audio, hidden_out=None, logits_out=None) -> None:
+    """prompts: sequence of (ids int array, audio_offset, audio_count);
+    audio: float32 CUDA tensor [sum counts, hidden] (or None when all counts
+    are 0); hidden_out / logits_out: float32 CUDA tensors or None."""
+    ids = np.ascontiguousarray(np.concatenate([np.asarray(p[0], dtype=np.int32) for p in prompts])
+                               if prompts else np.zeros(0, np.int32))
+    lens = np.ascontiguousarray([len(p[0]) for p in prompts], dtype=np.int64)
+    offs = np.ascontiguousarray([int(p[1]) for p in prompts], dtype=np.int64)
+    cnts = np.ascontiguousarray([int(p[2]) for p in prompts], dtype=np.int64)
+    H, V = t.dims.hidden, t.dims.vocab
+    A = int(cnts.sum()) if len(cnts) else 0
+
+    import torch
+
+    def dev(x, n, what):
+        if x is None:
+            return None
+        if not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous() or x.numel() < n:
+            raise QAError(QA_STATUS_INVALID_PARAMS, f"{what} must be a contiguous float32 device tensor of >= {n}")
+        return C.c_void_p(x.data_ptr())
+
+    pa = dev(audio, A * H, "audio") if A else None
+    ph = dev(hidden_out, int(lens.sum()) * H, "hidden_out")
+    pl = dev(logits_out, len(prompts) * V, "logits_out")
+    _check(_lib.qa_thinker_prefill(t.handle, ids.ctypes.data_as(C.POINTER(C.c_int32)),
+                                   lens.ctypes.data_as(C.POINTER(C.c_int64)), len(prompts), pa,
+                                   offs.ctypes.data_as(C.POINTER(C.c_int64)),
+                                   cnts.ctypes.data_as(C.POINTER(C.c_int64)), ph, pl))
+
+
+def thinker_prefill(t: Thinker, prompts, audio, want_hidden: bool = True, want_logits: bool = True):
+    """Allocate the outputs on audio's device (cuda:0 if audio is None) and prefill."""
+    import torch
+    devc = audio.device if audio is not None else torch.device("cuda:0")
+    T = sum(len(p[0]) for p in prompts)
+    h = torch.empty((T, t.dims.hidden), dtype=torch.float32, device=devc) if want_hidden else None
+    g = torch.empty((len(prompts), t.dims.vocab), dtype=torch.float32, device=devc) if want_logits else None
+    qa_thinker_prefill(t, prompts, audio, h, g)
+    return h, g

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqa_encoder.so")
-SOURCES = ["frontend.hip", "stem.hip", "gemm.hip", "norm_attn.hip", "resample.hip", "encoder.cpp"]
+SOURCES = ["frontend.hip", "stem.hip", "gemm.hip", "norm_attn.hip", "resample.hip", "thinker.hip", "encoder.cpp",
+           "thinker_host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

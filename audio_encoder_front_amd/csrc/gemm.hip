@@ -198,6 +198,32 @@ struct EpiF32Bias {        // out = acc + bias, fp32
     }
 };
 
+// SwiGLU of the Thinker FFN (qwenasr.cpp ARCHITECTURE.md, "Qwen3 Thinker
+// decoder": silu(gate) * up).  The gate and up weights are interleaved in
+// blocks of 16 rows (gate rows f..f+15, then up rows f..f+15, ...), so MFMA
+// column tiles 2k and 2k + 1 hold gate and up of the same 16 features and the
+// epilogue sees both in one lane: out[m][f] = silu(g) * u, f = 16 (n / 32) + n % 16.
+template <typename T>
+struct EpiSwiGLU {
+    T* out;
+    int M, F;
+    static constexpr bool kPaired = true;
+    __device__ f32x4 init(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ void pair(int m, int n, f32x4 g, f32x4 u) const {
+        const int f = 16 * (n / 32) + n % 16;
+        if (m >= M || f >= F) return;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = g[r] / (1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g[r])) * u[r];
+        store4(out + (size_t)m * F + f, v[0], v[1], v[2], v[3]);
+    }
+};
+
+template <class EP, class = void>
+struct EpiIsPaired { static constexpr bool value = false; };
+template <class EP>
+struct EpiIsPaired<EP, decltype((void)EP::kPaired)> { static constexpr bool value = EP::kPaired; };
+
 struct EpiPE {             // x = acc + pe[src[m] % 13]; tap = acc
     float* x;
     float* tap;
@@ -218,7 +244,8 @@ struct EpiPE {             // x = acc + pe[src[m] % 13]; tap = acc
 
 // Launch-site tags: one kernel symbol per call site, so profilers attribute
 // time per site.  The tag changes nothing in the generated code.
-enum Site { kQKV = 1, kFC1, kProj1, kOProj, kFC2, kProj2, kConv2, kConv3, kConvOut };
+enum Site { kQKV = 1, kFC1, kProj1, kOProj, kFC2, kProj2, kConv2, kConv3, kConvOut,
+            kTQKV, kTOProj, kTGateUp, kTDown, kTLogits };
 
 // Swizzled 16-byte column of K-chunk c in LDS row r: rows of 128 B hold 8
 // chunks (XOR with r % 8), rows of 64 B hold 4 (XOR with (r / 2) % 4); either
@@ -357,11 +384,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
         __syncthreads();
     }
     // acc[i][j] lane holds out[m = row fr][n = 4 fg + r] of tile (i, j)
+    if constexpr (EpiIsPaired<EP>::value) {
+        static_assert(TN % 2 == 0, "paired epilogue needs an even number of column tiles per wave");
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            ep(m0 + (wm * TM + i) * 16 + fr, n0 + (wn * TN + j) * 16 + 4 * fg, acc[i][j]);
+            for (int j = 0; j < TN; j += 2)
+                ep.pair(m0 + (wm * TM + i) * 16 + fr, n0 + (wn * TN + j) * 16 + 4 * fg, acc[i][j], acc[i][j + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                ep(m0 + (wm * TM + i) * 16 + fr, n0 + (wn * TN + j) * 16 + 4 * fg, acc[i][j]);
+    }
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int BKB, int SITE, class AL, class EP>
@@ -433,6 +469,28 @@ hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, in
     return run<kProj2>(s, al, M, w, N, K, ep);
 }
 
+template <typename T>
+hipError_t thinker_gemm(hipStream_t s, int site, const T* a, int M, int K, const T* w, int N,
+                        const float* zero, T* out_t, float* x) {
+    DenseA<T> al{a, M, K, K};
+    switch (site) {
+        case kTQKV: return run<kTQKV>(s, al, M, w, N, K, EpiBias<T>{out_t, zero, M, N, false});
+        case kTOProj: return run<kTOProj>(s, al, M, w, N, K, EpiResid{x, zero, M, N});
+        case kTDown: return run<kTDown>(s, al, M, w, N, K, EpiResid{x, zero, M, N});
+        case kTGateUp:
+            if (N % 32) return hipErrorInvalidValue;
+            return run<kTGateUp>(s, al, M, w, N, K, EpiSwiGLU<T>{out_t, M, N / 2});
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t thinker_logits(hipStream_t s, const T* a, const int* rows, int n_rows, int K, const T* w, int N,
+                          const float* zero, float* out) {
+    GatherA<T> al{a, rows, n_rows, K};
+    return run<kTLogits>(s, al, n_rows, w, N, K, EpiF32Bias{out, zero, n_rows, N});
+}
+
 #define QA_INST(T)                                                                                    \
     template hipError_t conv3x3s2<T>(hipStream_t, const T*, int, int, int, int, const T*, const float*, \
                                      T*, bool, bool);                                                 \
@@ -444,6 +502,14 @@ hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, in
                                            const float*, float*);                                     \
     template hipError_t gemm_bias_f32<T>(hipStream_t, const T*, int, int, const T*, int, const float*, \
                                          float*);
+template hipError_t thinker_gemm<float>(hipStream_t, int, const float*, int, int, const float*, int, const float*,
+                                        float*, float*);
+template hipError_t thinker_gemm<bf16>(hipStream_t, int, const bf16*, int, int, const bf16*, int, const float*,
+                                       bf16*, float*);
+template hipError_t thinker_logits<float>(hipStream_t, const float*, const int*, int, int, const float*, int,
+                                          const float*, float*);
+template hipError_t thinker_logits<bf16>(hipStream_t, const bf16*, const int*, int, int, const bf16*, int,
+                                         const float*, float*);
 QA_INST(float)
 QA_INST(bf16)
 

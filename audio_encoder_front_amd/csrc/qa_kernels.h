@@ -93,4 +93,26 @@ template <typename T>
 hipError_t attention(hipStream_t s, const T* qkv, const int* cu_seqlens, int n_windows, int n_heads,
                      int d, int max_len, T* out);
 
+// ---- Thinker prefill (audio splice, RMSNorm, QK-norm + RoPE, causal GQA)
+constexpr int kThinkerSiteQKV = 10, kThinkerSiteOProj = 11, kThinkerSiteGateUp = 12, kThinkerSiteDown = 13;
+template <typename T>
+hipError_t embed_splice(hipStream_t s, const T* embed, const float* audio, const int* src, int M, int H, float* x);
+template <typename T>
+hipError_t rmsnorm(hipStream_t s, const float* x, int M, int H, const float* g, float eps, T* out);
+template <typename T>
+hipError_t qknorm_rope(hipStream_t s, T* qkv, int M, int hq, int hkv, const int* pos, const float* qg,
+                       const float* kg, const float2* cs, float eps);
+template <typename T>
+hipError_t thinker_attention(hipStream_t s, const T* qkv, const int* cu, int n_prompts, int hq, int hkv,
+                             int max_len, T* out);
+// site kThinkerSiteQKV: out_t = a . w^T (no bias); kThinkerSiteOProj / Down: x += a . w^T;
+// kThinkerSiteGateUp: out_t[M][N/2] = silu(gate) * up with w rows interleaved in 16-row blocks.
+template <typename T>
+hipError_t thinker_gemm(hipStream_t s, int site, const T* a, int M, int K, const T* w, int N,
+                        const float* zero, T* out_t, float* x);
+// out[i][:] = a[rows[i]] . w^T (fp32), i < n_rows.
+template <typename T>
+hipError_t thinker_logits(hipStream_t s, const T* a, const int* rows, int n_rows, int K, const T* w, int N,
+                          const float* zero, float* out);
+
 }  // namespace qa

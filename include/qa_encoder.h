@@ -169,6 +169,82 @@ int qa_encoder_set_profiling_label(qa_encoder *e, const char *label);
 void qa_encoder_free(qa_encoder *e);
 
 /* ------------------------------------------------------------------------
+ * Audio splice + Qwen3 Thinker prefill, the step after the encoder
+ * (qwenasr.cpp ARCHITECTURE.md "Qwen3 Thinker decoder": per layer RMSNorm ->
+ * q/k/v projections -> per-head RMSNorm on q and k -> 1D NEOX RoPE (base 1e6)
+ * -> causal grouped-query attention -> output projection + residual; RMSNorm
+ * -> SwiGLU (silu(gate) * up) -> down projection + residual; final RMSNorm ->
+ * output projection tied to the token embedding; no bias anywhere.
+ * "Prompt assembly and audio splice": the prompt's id sequence is embedded,
+ * then the placeholder span is overwritten with the encoder states.)
+ * Readings where the page is silent: RMSNorm eps 1e-6; positions 0..T-1 of
+ * each prompt (prefill from an empty cache); each prompt of a packed batch
+ * attends only to itself.  Precision as for the encoder: bf16 operands at
+ * operator boundaries (the q/k after norm and RoPE, v, the attention output
+ * and the SwiGLU output included), fp32 accumulation, residual stream,
+ * RMSNorm statistics and softmax.
+ */
+typedef struct qa_thinker_dims {
+    int abi_version;   /* must equal QA_ABI_VERSION */
+    int hidden;        /* embedding_length: multiple of 64, <= 4096 (1024 / 2048 on the page) */
+    int n_layers;      /* block_count (28) */
+    int n_q_heads;     /* attention.head_count (16), a multiple of n_kv_heads, <= 64 */
+    int n_kv_heads;    /* attention.head_count_kv (8) */
+    int head_dim;      /* attention.key_length: must be 128 */
+    int ffn_dim;       /* feed_forward_length: multiple of 16 (3072 / 6144) */
+    int vocab;         /* vocab_size (151936) */
+    int dtype;         /* QA_DTYPE_F32 or QA_DTYPE_BF16 */
+} qa_thinker_dims;
+
+/* HOST pointers in PyTorch layouts (Linear = [out, in]), element type = dtype.
+ *   embed [vocab, hidden] (also the output projection);
+ *   per layer (arrays of n_layers pointers): attn_norm, ffn_norm [hidden];
+ *     q_w [n_q_heads 128, hidden]; k_w, v_w [n_kv_heads 128, hidden];
+ *     q_norm, k_norm [128]; o_w [hidden, n_q_heads 128];
+ *     gate_w, up_w [ffn, hidden]; down_w [hidden, ffn];
+ *   out_norm [hidden].
+ * Copied (and repacked) at create; the caller may free them afterwards. */
+typedef struct qa_thinker_weights {
+    const void *embed;
+    const void *const *attn_norm, *const *q_w, *const *k_w, *const *v_w, *const *q_norm, *const *k_norm;
+    const void *const *o_w, *const *ffn_norm, *const *gate_w, *const *up_w, *const *down_w;
+    const void *out_norm;
+} qa_thinker_weights;
+
+typedef struct qa_thinker qa_thinker;   /* opaque */
+
+/* Validate and copy the weights to the current HIP device.  NULL on failure
+ * (qa_last_error says why). */
+qa_thinker *qa_thinker_create(const qa_thinker_weights *w, const qa_thinker_dims *d);
+
+/* Enqueue later work of this handle on hip_stream (NULL = null stream). */
+int qa_thinker_set_stream(qa_thinker *t, void *hip_stream);
+
+/* Prefill a packed batch of n_prompts prompts.
+ *   ids            HOST int32 [sum lengths]: token ids, prompts in order (ids
+ *                  inside an audio span are ignored; others must be < vocab).
+ *   lengths        HOST int64 [n_prompts], each 1..65536 (context_length).
+ *   audio          DEVICE float32 [sum audio_counts x hidden]: the encoder
+ *                  states spliced into the prompts, in prompt order (e.g. the
+ *                  output of qa_encode with output_dim == hidden).  Caller-owned.
+ *   audio_offsets, audio_counts
+ *                  HOST int64 [n_prompts]: the placeholder span of each prompt
+ *                  (0 <= offset, offset + count <= length).
+ *   hidden_out     DEVICE float32 [sum lengths x hidden] or NULL: the hidden
+ *                  states after the final RMSNorm.
+ *   logits_out     DEVICE float32 [n_prompts x vocab] or NULL: the logits of
+ *                  each prompt's last token.
+ * Argument checks happen before any device work; the call synchronises the
+ * handle's stream before it returns.  Returns QA_STATUS_OK, INVALID_PARAMS,
+ * OOM or ENCODE_FAILED (launch error).  Calls on one handle must not overlap. */
+int qa_thinker_prefill(qa_thinker *t, const int32_t *ids, const int64_t *lengths, int n_prompts,
+                       const float *audio, const int64_t *audio_offsets, const int64_t *audio_counts,
+                       float *hidden_out, float *logits_out);
+
+/* Release device memory and the handle.  NULL is a no-op. */
+void qa_thinker_free(qa_thinker *t);
+
+/* ------------------------------------------------------------------------
  * Resampling to 16 kHz, the step in front of the front end (qwenasr.cpp
  * ARCHITECTURE.md "Upstream model": any input is resampled to 16 kHz mono
  * before the frontend; "Module map": a Kaiser polyphase resampler).  The page

@@ -79,6 +79,28 @@ int main(void) {
     CHECK(qa_resample(NULL, NULL, NULL, 10, NULL) == QA_STATUS_INVALID_PARAMS);
     qa_resampler_free(NULL);
 
+    /* Thinker prefill: argument checks only */
+    {
+        qa_thinker_dims td;
+        qa_thinker_weights tw;
+        int32_t tid[2] = {1, 2};
+        int64_t tl[1] = {2}, to[1] = {0}, tc[1] = {0};
+        memset(&td, 0, sizeof td);
+        memset(&tw, 0, sizeof tw);
+        td.abi_version = QA_ABI_VERSION; td.hidden = 2048; td.n_layers = 28; td.n_q_heads = 16; td.n_kv_heads = 8;
+        td.head_dim = 128; td.ffn_dim = 6144; td.vocab = 151936; td.dtype = QA_DTYPE_BF16;
+        CHECK(qa_thinker_create(&tw, &td) == NULL);          /* NULL weight pointers */
+        CHECK(qa_thinker_create(NULL, &td) == NULL);
+        td.head_dim = 64;
+        CHECK(qa_thinker_create(&tw, &td) == NULL);
+        CHECK(strstr(qa_last_error(), "head_dim") != NULL);
+        td.head_dim = 128; td.n_kv_heads = 5;
+        CHECK(qa_thinker_create(&tw, &td) == NULL);
+        CHECK(qa_thinker_prefill(NULL, tid, tl, 1, NULL, to, tc, NULL, NULL) == QA_STATUS_INVALID_PARAMS);
+        CHECK(qa_thinker_set_stream(NULL, NULL) == QA_STATUS_INVALID_PARAMS);
+        qa_thinker_free(NULL);
+    }
+
     if (fails) return 1;
     printf("abi_c: all checks passed\n");
     return 0;
