@@ -112,7 +112,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* __restrict__ qkv, i
 // Per key block of 64: S^T = K Q^T on MFMA (a lane holds one query column),
 // the causal mask, an online softmax (running max / sum, the partial output
 // rescaled when the max grows) and O^T = V^T P^T with V^T transposed in LDS;
-// the workgroup stops at the block holding its last query.
+// the workgroup stops at the block holding its last query.  When a KV head
+// serves an even number of query heads, a workgroup takes two of them (8
+// waves) so each K/V block is staged once for both.
 constexpr int kTHd = 128;
 constexpr int kTKB = 64;                     // keys per block
 
@@ -154,30 +156,35 @@ __device__ __forceinline__ void tpv_step(float, const char* vt, int kbase, int f
     }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void thinker_attention_kernel(const T* __restrict__ qkv,
-                                                                const int* __restrict__ cu, int hq, int hkv,
-                                                                int qgroups, T* __restrict__ out) {
+template <typename T, int HPW>
+__global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* __restrict__ qkv,
+                                                                      const int* __restrict__ cu, int hq, int hkv,
+                                                                      int qgroups, T* __restrict__ out) {
     constexpr int KR = TAttnLds<T>::krow, VR = TAttnLds<T>::vrow;
     constexpr int PER = Elem<T>::per16;
     constexpr int CPR = kTHd / PER;                          // 16-byte chunks per head row
     constexpr int KBN = kTHd * (int)sizeof(T) / 64;          // 64-byte MFMA K blocks per head row
-    constexpr int NCH = kTKB * CPR / 256;                    // chunks per thread per key block
+    constexpr int NT = 256 * HPW;                            // threads
+    constexpr int NCH = kTKB * CPR / NT;                     // chunks per thread per key block
     __shared__ __align__(16) char ks[kTKB * KR];
     __shared__ __align__(16) char vts[kTHd * VR];
 
+    // workgroup = (prompt, HPW consecutive query heads of one KV head, 64 queries);
+    // waves 4 i .. 4 i + 3 take query head i of the group, 16 queries each
     const int qg = blockIdx.x % qgroups;
     const int ph = blockIdx.x / qgroups;
-    const int seg = ph / hq, h = ph % hq;
-    const int kvh = h / (hq / hkv);
+    const int hgroups = hq / HPW;
+    const int seg = ph / hgroups;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = (ph % hgroups) * HPW + (wave >> 2);
+    const int kvh = h / (hq / hkv);                          // the same for all HPW heads
     const int s0 = cu[seg], n = cu[seg + 1] - s0;
     if (qg * 64 >= n) return;                                // whole workgroup idle (uniform)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int fr = lane & 15, fg = lane >> 4;
     const size_t ld = (size_t)(hq + 2 * hkv) * kTHd;
     const T* kbase_p = qkv + (size_t)hq * kTHd + (size_t)kvh * kTHd;
     const T* vbase_p = kbase_p + (size_t)hkv * kTHd;
-    const int qt = qg * 4 + wave;
+    const int qt = qg * 4 + (wave & 3);
     const bool active = qt * 16 < n;                         // wave-uniform
     const int q = qt * 16 + fr;                              // this lane's query (within the prompt)
     uint4 qf[KBN];
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(256) void thinker_attention_kernel(const T* __restr
         uint4 kv[NCH], vv[NCH];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int idx = tid + c * 256;
+            const int idx = tid + c * NT;
             const int t = idx / CPR, ch = idx % CPR;
             kv[c] = vv[c] = zero16();
             if (k0 + t < n) {
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(256) void thinker_attention_kernel(const T* __restr
         }
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int idx = tid + c * 256;
+            const int idx = tid + c * NT;
             const int t = idx / CPR, ch = idx % CPR;
             st16(ks + t * KR + ch * 16, kv[c]);
             const T* ve = reinterpret_cast<const T*>(&vv[c]);
@@ -232,27 +239,37 @@ __global__ __launch_bounds__(256) void thinker_attention_kernel(const T* __restr
         }
         // lane holds S^T[key k0 + 16 kt + 4 fg + r][query fr]
         float bm = -INFINITY;
+        if (k0 + kTKB - 1 <= qt * 16 && k0 + kTKB <= n) {   // whole block visible to every query of the wave
 #pragma unroll
-        for (int kt = 0; kt < kTKB / 16; ++kt)
+            for (int kt = 0; kt < kTKB / 16; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + kt * 16 + 4 * fg + r;
-                const float v = (key <= q && key < n) ? sacc[kt][r] * sc : -INFINITY;
-                sacc[kt][r] = v;
-                bm = fmaxf(bm, v);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    sacc[kt][r] *= sc;
+                    bm = fmaxf(bm, sacc[kt][r]);
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < kTKB / 16; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = k0 + kt * 16 + 4 * fg + r;
+                    const float v = (key <= q && key < n) ? sacc[kt][r] * sc : -INFINITY;
+                    sacc[kt][r] = v;
+                    bm = fmaxf(bm, v);
+                }
+        }
         bm = fmaxf(bm, __shfl_xor(bm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
         const float mn = fmaxf(m, bm);
         // a query past the prompt end (q >= n) sees no key: keep it finite
         const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = exp2f(m - mref);
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
         float bs = 0.f;
 #pragma unroll
         for (int kt = 0; kt < kTKB / 16; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = exp2f(sacc[kt][r] - mref);
+                const float p = __builtin_amdgcn_exp2f(sacc[kt][r] - mref);
                 sacc[kt][r] = p;
                 bs += p;
             }
@@ -319,9 +336,14 @@ hipError_t thinker_attention(hipStream_t s, const T* qkv, const int* cu, int n_p
     if (n_prompts <= 0) return hipSuccess;
     if (hkv <= 0 || hq % hkv) return hipErrorInvalidValue;
     const int qgroups = (max_len + 63) / 64;
-    const int64_t blocks = (int64_t)n_prompts * hq * qgroups;
+    // two query heads of one KV head per workgroup when the group size is even
+    const int hpw = (hq / hkv) % 2 == 0 ? 2 : 1;
+    const int64_t blocks = (int64_t)n_prompts * (hq / hpw) * qgroups;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    thinker_attention_kernel<T><<<(unsigned)blocks, 256, 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
+    if (hpw == 2)
+        thinker_attention_kernel<T, 2><<<(unsigned)blocks, 512, 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
+    else
+        thinker_attention_kernel<T, 1><<<(unsigned)blocks, 256, 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
     return hipGetLastError();
 }
 

@@ -134,6 +134,47 @@ def resample_bench(dev, rate: int = 44100, seconds: int = 1200, reps: int = 10):
             "bound": "hbm", "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
 
 
+def thinker_bench(dev, enc_out, wl, reps: int = 3):
+    """The step after the encoder, timed on its own (not part of `value`): the
+    Thinker of the same model size prefilling one prompt whose placeholder
+    span is the encoder output just computed (all clips' states in one span)."""
+    import numpy as np
+    import torch
+    import audio_encoder_front_amd as qa
+    import synth.thinker as ST
+    dims = ST.THINKER_17B if wl.dims.output_dim == ST.THINKER_17B.hidden else ST.THINKER_06B
+    if enc_out.shape[1] != dims.hidden:
+        return None
+    W = ST.make_weights(dims, 317)
+    t = qa.qa_thinker_create(W, dims)
+    del W
+    stream = torch.cuda.current_stream(dev)
+    qa.qa_thinker_set_stream(t, stream)
+    S = enc_out.shape[0]
+    ids, off = ST.make_prompt(S, dims.vocab, [318, 0])
+    prompts = [(ids, off, S)]
+    T = len(ids)
+    h = torch.empty((T, dims.hidden), dtype=torch.float32, device=dev)
+    g = torch.empty((1, dims.vocab), dtype=torch.float32, device=dev)
+    qa.qa_thinker_prefill(t, prompts, enc_out, h, g)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        qa.qa_thinker_prefill(t, prompts, enc_out, h, g)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    t.free()
+    H, F, hq, hkv, L = dims.hidden, dims.ffn_dim, dims.n_q_heads, dims.n_kv_heads, dims.n_layers
+    gemm = 2.0 * T * (H * (hq + 2 * hkv) * 128 + hq * 128 * H + 2 * H * F + F * H) * L
+    attn = 4.0 * (T * (T + 1) / 2) * 128 * hq * L          # QK^T and PV over the causal triangle
+    flops = gemm + attn + 2.0 * H * dims.vocab
+    return {"workload": f"{H}-hidden Thinker ({L} layers, {hq}/{hkv} heads of 128, FFN {F}) prefill of one "
+                        f"prompt splicing the {S} encoder states ({T} tokens)",
+            "avg_ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "flops": flops,
+            "mfma_frac": round(flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)}
+
+
 def cpu_baseline(wl, seconds: float):
     """The fp64 oracle on the first `seconds` of the workload's first clip."""
     import numpy as np
@@ -163,6 +204,7 @@ def main():
     ap.add_argument("--workload", default="b17_20m")
     ap.add_argument("--cpu-sample-s", type=float, default=240.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-thinker", action="store_true", help="skip the Thinker-prefill line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -265,6 +307,8 @@ def main():
                         "the timed steps carry events only around the dominant kernel",
     }
     res["resample"] = resample_bench(dev)
+    if not args.no_thinker:
+        res["thinker_prefill"] = thinker_bench(dev, out, wl)
     if args.calibrate_copy:
         copy_calibration()
     if not args.no_cpu_baseline:
