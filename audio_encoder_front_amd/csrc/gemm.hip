@@ -37,49 +37,76 @@ __device__ __align__(16) uint4 g_zero16[2];
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// global_load_lds_dwordx4 written as inline asm: the compiler's wait-count
-// pass cannot tell the two LDS stages apart and would otherwise wait for the
+// Direct-to-LDS loads written as inline asm: the compiler's wait-count pass
+// cannot tell the two LDS stages apart and would otherwise wait for the
 // in-flight stage k+1 loads before every LDS read of stage k.  Completion is
 // awaited explicitly (s_waitcnt vmcnt(0)) before the barrier that publishes
 // a stage.  M0 carries the wave's LDS destination; no other code in these
 // kernels uses M0.
-__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
-    const unsigned base = __builtin_amdgcn_readfirstlane(
-        (unsigned)(uintptr_t)(lds_void*)lds_wave_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "m0");
+//
+// Two forms.  buffer_load_dwordx4 ... lds reads through a buffer resource
+// (base and size in four SGPRs) at a 32-bit lane offset: one VGPR per load
+// and no 64-bit address arithmetic, and any offset at or past the resource
+// size reads zeros, which covers ragged rows and conv padding for free.  The
+// loaders that can keep their per-workgroup range under 4 GB (dense rows, conv
+// chunks) use it; the row-gather loader uses global_load_lds_dwordx4 with
+// 64-bit addresses and a zero block.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr unsigned kOobOffset = 0xFFFFFFF0u;     // >= every resource size below: reads zeros
+
+__device__ __forceinline__ void dma16(const void* src, unsigned lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "m0");
+}
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, unsigned voff, unsigned lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff),
+                 "s"(rsrc) : "m0");
+}
+// Raw buffer resource (stride 0) over [base, base + bytes), bytes clamped
+// below kOobOffset; the fourth word is the gfx9 raw-buffer format.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint64_t bytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const unsigned n = bytes < 0xFFFFFF00ull ? (unsigned)bytes : 0xFFFFFF00u;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)n);
+    r[3] = 0x00020000;
+    return r;
 }
 
 // ------------------------------------------------------------ A loaders
 // A loader keeps a compact per-lane state for the AI rows the lane fetches
-// (rows r, r + 8, ..., r + 8 (AI-1) of the tile); kprep(k0) is evaluated once
-// per stage; addr(lane, q, kx) gives the source of elements [k0, k0 + per16)
-// of row q, or g_zero16 outside the matrix.
+// (rows r, r + RS, ..., r + RS (AI-1) of the tile); kprep(k0) is evaluated
+// once per stage.  Buffer loaders (kBuffer) give rsrc(tile0), the workgroup's
+// resource, and boff(lane, q, kx), the byte offset of elements [k0, k0 + per16)
+// of row q or kOobOffset outside the matrix; the gather loader gives
+// addr(lane, q, kx), a global address or g_zero16.
 
 template <typename T>
 struct DenseA {
+    static constexpr bool kBuffer = true;
     const T* a;
     int M, K, lda;
     template <int AI, int RS>
-    struct Lane { const char* base; unsigned valid; };
-    struct KCtx { int off; bool ok; };
-    template <int AI, int RS>
-    __device__ Lane<AI, RS> init(int m) const {
-        Lane<AI, RS> l{reinterpret_cast<const char*>(a + (size_t)m * lda), 0u};
-#pragma unroll
-        for (int q = 0; q < AI; ++q) l.valid |= (m + RS * q < M ? 1u : 0u) << q;
-        return l;
+    struct Lane { unsigned off; };             // byte offset of the lane's first row from row tile0
+    struct KCtx { unsigned off; bool ok; };
+    __device__ i32x4 rsrc(int tile0) const {
+        return buffer_rsrc(a + (size_t)tile0 * lda, (uint64_t)(M > tile0 ? M - tile0 : 0) * lda * sizeof(T));
     }
-    __device__ KCtx kprep(int k0) const { return KCtx{k0 * (int)sizeof(T), k0 < K}; }
     template <int AI, int RS>
-    __device__ const void* addr(const Lane<AI, RS>& l, int q, const KCtx& k) const {
-        return (((l.valid >> q) & 1u) && k.ok)
-                   ? (const void*)(l.base + (size_t)q * RS * lda * sizeof(T) + k.off)
-                   : (const void*)g_zero16;
+    __device__ Lane<AI, RS> init(int tile0, int m) const {
+        return Lane<AI, RS>{(unsigned)((m - tile0) * lda * (int)sizeof(T))};
+    }
+    __device__ KCtx kprep(int k0) const { return KCtx{(unsigned)(k0 * (int)sizeof(T)), k0 < K}; }
+    template <int AI, int RS>
+    __device__ unsigned boff(const Lane<AI, RS>& l, int q, const KCtx& k) const {
+        return k.ok ? l.off + (unsigned)(q * RS * lda * (int)sizeof(T)) + k.off : kOobOffset;
     }
 };
 
 template <typename T>
 struct GatherA {   // row m of the GEMM is row src[m] of a
+    static constexpr bool kBuffer = false;
     const T* a;
     const int* src;
     int M, K;
@@ -87,7 +114,7 @@ struct GatherA {   // row m of the GEMM is row src[m] of a
     struct Lane { int row[AI]; };
     struct KCtx { int off; bool ok; };
     template <int AI, int RS>
-    __device__ Lane<AI, RS> init(int m) const {
+    __device__ Lane<AI, RS> init(int, int m) const {
         Lane<AI, RS> l;
 #pragma unroll
         for (int q = 0; q < AI; ++q) l.row[q] = m + RS * q < M ? src[m + RS * q] : -1;
@@ -104,19 +131,28 @@ struct GatherA {   // row m of the GEMM is row src[m] of a
 
 template <typename T>
 struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
+    static constexpr bool kBuffer = true;
     const T* in;
     int M, Hin, Win, C, Hout, Wout;
     bool time_major;                  // output row order (chunk, j, i) instead of (chunk, i, j)
     // Input layout per chunk: NHWC [Hin][Win][C] (pstride = C, cbstride = 32) or
     // channel-blocked [C / 32][Hin][Win][32] (pstride = 32, cbstride = Hin Win 32).
     int pstride, cbstride;
+    // A tile of up to 256 output rows touches at most 3 chunks, so offsets from
+    // the tile's first chunk stay far below 4 GB.
     template <int AI, int RS>
-    struct Lane { int chunk[AI]; int rc[AI]; };   // rc = (2i-1) << 16 | (2j-1) & 0xffff
-    struct KCtx { int a, b, off; bool ok; };
+    struct Lane { int cofs[AI]; int rc[AI]; };    // chunk offset (elements) from the tile's first chunk, or -1;
+                                                  // rc = (2i-1) << 16 | (2j-1) & 0xffff
+    struct KCtx { int a, b; unsigned off; bool ok; };
+    __device__ int chunk_elems() const { return Hin * Win * C; }
+    __device__ i32x4 rsrc(int tile0) const {
+        const int per = Hout * Wout, c0 = tile0 / per, nch = M / per;
+        return buffer_rsrc(in + (size_t)c0 * chunk_elems(), (uint64_t)(nch - c0) * chunk_elems() * sizeof(T));
+    }
     template <int AI, int RS>
-    __device__ Lane<AI, RS> init(int m0) const {
+    __device__ Lane<AI, RS> init(int tile0, int m0) const {
         Lane<AI, RS> l;
-        const int per = Hout * Wout;
+        const int per = Hout * Wout, c0 = tile0 / per;
 #pragma unroll
         for (int q = 0; q < AI; ++q) {
             const int m = m0 + RS * q;
@@ -124,7 +160,7 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
             int i, j;
             if (time_major) { j = rem / Hout; i = rem - j * Hout; }
             else            { i = rem / Wout; j = rem - i * Wout; }
-            l.chunk[q] = m < M ? chunk : -1;
+            l.cofs[q] = m < M ? (chunk - c0) * chunk_elems() : -1;
             l.rc[q] = ((2 * i - 1) << 16) | ((2 * j - 1) & 0xffff);
         }
         return l;
@@ -136,16 +172,15 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
         const int cb = k0 / (9 * kConvCB), rem = k0 - cb * (9 * kConvCB);
         const int tap = rem / kConvCB, ci = cb * kConvCB + (rem - tap * kConvCB);
         const int a = tap / 3;
-        return KCtx{a, tap - 3 * a, (cb * cbstride + (ci - cb * kConvCB)) * (int)sizeof(T), k0 < 9 * C};
+        return KCtx{a, tap - 3 * a, (unsigned)((cb * cbstride + (ci - cb * kConvCB)) * (int)sizeof(T)), k0 < 9 * C};
     }
     template <int AI, int RS>
-    __device__ const void* addr(const Lane<AI, RS>& l, int q, const KCtx& k) const {
+    __device__ unsigned boff(const Lane<AI, RS>& l, int q, const KCtx& k) const {
         const int r = (l.rc[q] >> 16) + k.a;
         const int col = (int)(short)(l.rc[q] & 0xffff) + k.b;
-        if (l.chunk[q] < 0 || !k.ok || (unsigned)r >= (unsigned)Hin || (unsigned)col >= (unsigned)Win)
-            return g_zero16;
-        return reinterpret_cast<const char*>(in + (size_t)l.chunk[q] * Hin * Win * C + (size_t)(r * Win + col) * pstride) +
-               k.off;
+        if (l.cofs[q] < 0 || !k.ok || (unsigned)r >= (unsigned)Hin || (unsigned)col >= (unsigned)Win)
+            return kOobOffset;
+        return (unsigned)((l.cofs[q] + (r * Win + col) * pstride) * (int)sizeof(T)) + k.off;
     }
 };
 
@@ -296,20 +331,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     // l % CPR, so it fetches the chunk that the swizzle puts there.
     const int lrow = lane / CPR;
     const int kc = swz<BKB>(lrow, lane % CPR);
-    const auto alane = al.template init<AI, RPD>(m0 + wave * AI * RPD + lrow);
+    const auto alane = al.template init<AI, RPD>(m0, m0 + wave * AI * RPD + lrow);
     const DenseA<T> wl{w, N, K, K};
-    const auto wlane = wl.template init<BI, RPD>(n0 + wave * BI * RPD + lrow);
+    const auto wlane = wl.template init<BI, RPD>(n0, n0 + wave * BI * RPD + lrow);
+    i32x4 ra = {0, 0, 0, 0};
+    if constexpr (AL::kBuffer) ra = al.rsrc(m0);
+    const i32x4 rw = wl.rsrc(n0);
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_void*)smem;
+    const unsigned wave_u = (unsigned)__builtin_amdgcn_readfirstlane(wave);
     constexpr int KSTEP = BKB / (int)sizeof(T);   // K elements per stage
     auto issue = [&](int kt, int buf) {
         const int k0 = kt * KSTEP + kc * PER;
         const auto kx = al.kprep(k0);
         const auto kw = wl.kprep(k0);
-        char* sa = smem + buf * STAGE + wave * AI * 1024;
-        char* sb = smem + buf * STAGE + BM * BKB + wave * BI * 1024;
+        const unsigned sa = lds0 + buf * STAGE + wave_u * (AI * 1024);
+        const unsigned sb = lds0 + buf * STAGE + BM * BKB + wave_u * (BI * 1024);
 #pragma unroll
-        for (int q = 0; q < AI; ++q) dma16(al.addr(alane, q, kx), sa + q * 1024);
+        for (int q = 0; q < AI; ++q) {
+            if constexpr (AL::kBuffer) dma16_buf(ra, al.boff(alane, q, kx), sa + q * 1024);
+            else dma16(al.addr(alane, q, kx), sa + q * 1024);
+        }
 #pragma unroll
-        for (int q = 0; q < BI; ++q) dma16(wl.addr(wlane, q, kw), sb + q * 1024);
+        for (int q = 0; q < BI; ++q) dma16_buf(rw, wl.boff(wlane, q, kw), sb + q * 1024);
     };
 
     const int nk = (K + KSTEP - 1) / KSTEP;
