@@ -15,19 +15,19 @@
 // tile in stages of 128 bytes of K (64 bf16 or 32 fp32 elements).
 //
 // Staging: every 16-byte chunk moves global -> LDS with one direct-to-LDS
-// load (global_load_lds_dwordx4), no register round trip.  Such a load
-// writes 64 lanes x 16 B contiguously, i.e. 8 LDS rows of 128 B; lane l
-// therefore fetches K-chunk (l%8) ^ (row%8) of its row, an XOR swizzle that
-// makes the 16-byte fragment reads of 8 consecutive rows hit 8 different
-// 16-byte bank groups.  Chunks outside the matrix (ragged M/N/K, conv
-// padding) are fetched from a 16-byte zero block.  Two LDS stages: loads of
-// stage k+1 run while stage k is multiplied.
+// load, no register round trip.  Such a load writes 64 lanes x 16 B
+// contiguously, i.e. 8 LDS rows of 128 B; lane l therefore fetches K-chunk
+// (l%8) ^ (row%8) of its row, an XOR swizzle that makes the 16-byte fragment
+// reads of 8 consecutive rows hit 8 different 16-byte bank groups.  Chunks
+// outside the matrix (ragged M/N/K, conv padding) read as zeros.  Two LDS
+// stages: loads of stage k+1 run while stage k is multiplied.
 //
 // The MFMA is issued transposed (weights as the A operand): lane l then holds
-// 4 consecutive output columns of one output row, so bias loads and stores
-// are 8/16-byte vectors.  Workgroups are remapped so that each of the 8 XCDs
-// works through a contiguous, M-grouped range of tiles (L2 reuse of both
-// operand tiles).
+// 4 consecutive output columns of one output row.  After the K loop the tile
+// is staged row-major through LDS and written as whole rows (see the
+// epilogues).  Workgroups are remapped so that each of the 8 XCDs works
+// through a contiguous, M-grouped range of tiles (L2 reuse of both operand
+// tiles).
 #include "qa_device.h"
 #include "qa_kernels.h"
 
@@ -187,49 +187,102 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
 // ------------------------------------------------------------ epilogues
 // op(m, n, v): v holds out[m][n..n+3] before bias; n is a multiple of 4.
 
-template <typename T>
-struct EpiBias {           // out = acc + bias (optionally GELU), stored as T
+// Epilogues.  Every epilogue but EpiPE is "staged": after the K loop the
+// workgroup converts its accumulators (frag / pair), writes them row-major
+// into the idle LDS stages and then streams whole rows out with 16-byte
+// stores (row), so a wave writes 1 KB of contiguous rows per instruction
+// instead of 16 scattered 32-byte pieces.  S is the staged element type,
+// kDiv the ratio of accumulator columns to staged columns.  Bias terms are
+// folded into the accumulators' initial value (init) where the staged value
+// already includes them.
+
+// 4 consecutive fp32 values of v[n..n+3]; entries at or past N read as 0.
+__device__ __forceinline__ f32x4 load4_tail(const float* v, int n, int N) {
+    if (n + 4 <= N) {
+        const float4 b = *reinterpret_cast<const float4*>(v + n);
+        return f32x4{b.x, b.y, b.z, b.w};
+    }
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 4 && n + e < N; ++e) r[e] = v[n + e];
+    return r;
+}
+
+// Store the 16-byte staged chunk c (elements of type S) at p; only the first
+// `valid` elements when the chunk runs past the end of the row.
+template <typename S>
+__device__ __forceinline__ void store_chunk(S* p, uint4 c, int valid) {
+    constexpr int E = Elem<S>::per16;
+    if (valid >= E) { st16(p, c); return; }
+    const S* e = reinterpret_cast<const S*>(&c);
+    for (int i = 0; i < valid; ++i) p[i] = e[i];
+}
+
+template <typename T, bool kGelu>
+struct EpiBias {           // out = acc + bias (GELU if kGelu), stored as T
+    using S = T;
+    static constexpr bool kStaged = true;
+    static constexpr int kDiv = 1;
     T* out;
     const float* bias;
     int M, N;
-    bool gelu;
-    __device__ f32x4 init(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-    __device__ void operator()(int m, int n, f32x4 v) const {
-        if (m >= M || n >= N) return;
-        const float4 b = *reinterpret_cast<const float4*>(bias + n);
-        float x0 = v[0] + b.x, x1 = v[1] + b.y, x2 = v[2] + b.z, x3 = v[3] + b.w;
-        if (gelu) { x0 = gelu_erf(x0); x1 = gelu_erf(x1); x2 = gelu_erf(x2); x3 = gelu_erf(x3); }
-        store4(out + (size_t)m * N + n, x0, x1, x2, x3);
+    __device__ f32x4 init(int n) const { return n < N ? load4_tail(bias, n, N) : f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ void frag(f32x4 v, float* o) const {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = kGelu ? gelu_erf(v[r]) : v[r];
+    }
+    __device__ uint4 pre(int, int) const { return zero16(); }
+    __device__ void row(int m, int n, uint4 c, uint4) const {
+        if (m < M && n < N) store_chunk(out + (size_t)m * N + n, c, N - n);
     }
 };
 
 struct EpiResid {          // x = x + bias + acc (fp32 residual stream)
+    using S = float;
+    static constexpr bool kStaged = true;
+    static constexpr int kDiv = 1;
     float* x;
     const float* bias;
     int M, N;
-    // The accumulators start from x + bias (read before the K loop, so the
-    // read overlaps the first stages instead of a read-modify-write at the end).
-    __device__ f32x4 init(int m, int n) const {
-        if (m >= M || n >= N) return f32x4{0.f, 0.f, 0.f, 0.f};
-        const float4 b = *reinterpret_cast<const float4*>(bias + n);
-        const float4 r = *reinterpret_cast<const float4*>(x + (size_t)m * N + n);
-        return f32x4{r.x + b.x, r.y + b.y, r.z + b.z, r.w + b.w};
+    __device__ f32x4 init(int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ void frag(f32x4 v, float* o) const {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = v[r];
     }
-    __device__ void operator()(int m, int n, f32x4 v) const {
+    // The residual is read in whole rows per wave by pre(), issued for a
+    // band before its values are staged so the loads overlap the staging.
+    __device__ uint4 pre(int m, int n) const {
+        if (m >= M || n >= N) return zero16();
+        return __builtin_bit_cast(uint4, load4_tail(x + (size_t)m * N, n, N));
+    }
+    __device__ void row(int m, int n, uint4 c, uint4 pv) const {
         if (m >= M || n >= N) return;
-        store4(x + (size_t)m * N + n, v[0], v[1], v[2], v[3]);
+        float* p = x + (size_t)m * N + n;
+        const f32x4 a = __builtin_bit_cast(f32x4, c), r = __builtin_bit_cast(f32x4, pv);
+        const f32x4 b = load4_tail(bias, n, N);
+        if (n + 4 <= N) {
+            *reinterpret_cast<float4*>(p) = make_float4(r[0] + (b[0] + a[0]), r[1] + (b[1] + a[1]), r[2] + (b[2] + a[2]),
+                                                        r[3] + (b[3] + a[3]));
+        } else {
+            for (int e = 0; n + e < N; ++e) p[e] = r[e] + (b[e] + a[e]);
+        }
     }
 };
 
 struct EpiF32Bias {        // out = acc + bias, fp32
+    using S = float;
+    static constexpr bool kStaged = true;
+    static constexpr int kDiv = 1;
     float* out;
     const float* bias;
     int M, N;
-    __device__ f32x4 init(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-    __device__ void operator()(int m, int n, f32x4 v) const {
-        if (m >= M || n >= N) return;
-        const float4 b = *reinterpret_cast<const float4*>(bias + n);
-        store4(out + (size_t)m * N + n, v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w);
+    __device__ f32x4 init(int n) const { return n < N ? load4_tail(bias, n, N) : f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ void frag(f32x4 v, float* o) const {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = v[r];
+    }
+    __device__ uint4 pre(int, int) const { return zero16(); }
+    __device__ void row(int m, int n, uint4 c, uint4) const {
+        if (m < M && n < N) store_chunk(out + (size_t)m * N + n, c, N - n);
     }
 };
 
@@ -240,17 +293,20 @@ struct EpiF32Bias {        // out = acc + bias, fp32
 // epilogue sees both in one lane: out[m][f] = silu(g) * u, f = 16 (n / 32) + n % 16.
 template <typename T>
 struct EpiSwiGLU {
+    using S = T;
+    static constexpr bool kStaged = true;
+    static constexpr bool kPaired = true;
+    static constexpr int kDiv = 2;
     T* out;
     int M, F;
-    static constexpr bool kPaired = true;
-    __device__ f32x4 init(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-    __device__ void pair(int m, int n, f32x4 g, f32x4 u) const {
-        const int f = 16 * (n / 32) + n % 16;
-        if (m >= M || f >= F) return;
-        float v[4];
+    __device__ f32x4 init(int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ void pair(f32x4 g, f32x4 u, float* o) const {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = g[r] / (1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g[r])) * u[r];
-        store4(out + (size_t)m * F + f, v[0], v[1], v[2], v[3]);
+        for (int r = 0; r < 4; ++r) o[r] = g[r] / (1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g[r])) * u[r];
+    }
+    __device__ uint4 pre(int, int) const { return zero16(); }
+    __device__ void row(int m, int f, uint4 c, uint4) const {
+        if (m < M && f < F) store_chunk(out + (size_t)m * F + f, c, F - f);
     }
 };
 
@@ -259,13 +315,14 @@ struct EpiIsPaired { static constexpr bool value = false; };
 template <class EP>
 struct EpiIsPaired<EP, decltype((void)EP::kPaired)> { static constexpr bool value = EP::kPaired; };
 
-struct EpiPE {             // x = acc + pe[src[m] % 13]; tap = acc
+struct EpiPE {             // x = acc + pe[src[m] % 13]; tap = acc (stored from the lanes)
+    static constexpr bool kStaged = false;
     float* x;
     float* tap;
     const float* pe;
     const int* src;
     int M, N;
-    __device__ f32x4 init(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ f32x4 init(int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ void operator()(int m, int n, f32x4 v) const {
         if (m >= M || n >= N) return;
         const int j = src[m] % kChunkTok;
@@ -360,12 +417,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     const int fr = lane & 15, fg = lane >> 4;
     f32x4 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j) {
+        const f32x4 a0 = ep.init(n0 + (wn * TN + j) * 16 + 4 * fg);   // per output column
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            acc[i][j] = ep.init(m0 + (wm * TM + i) * 16 + fr, n0 + (wn * TN + j) * 16 + 4 * fg);
+        for (int i = 0; i < TM; ++i) acc[i][j] = a0;
+    }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // vmcnt(0) through the builtin, not inline asm: the compiler then knows
+    // that the accumulator initial values loaded above have landed, and does
+    // not wait for vector memory (i.e. for the next stage's loads) at the top
+    // of every K-loop iteration.
+    __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0), expcnt and lgkmcnt untouched
     __syncthreads();
     int sw[KB];
 #pragma unroll
@@ -427,13 +489,58 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
         __syncthreads();
     }
     // acc[i][j] lane holds out[m = row fr][n = 4 fg + r] of tile (i, j)
-    if constexpr (EpiIsPaired<EP>::value) {
-        static_assert(TN % 2 == 0, "paired epilogue needs an even number of column tiles per wave");
+    if constexpr (EP::kStaged) {
+        // Staged epilogue: the lanes write their converted values row-major
+        // into the two (now idle) LDS stages, rows of RB bytes whose 16-byte
+        // chunks are XOR-swizzled by row (conflict-free writes from 16 rows
+        // at once and conflict-free row reads); then every thread stores
+        // whole 16-byte chunks of consecutive rows.  A tile whose staged rows
+        // exceed the LDS goes out in PASSES bands of wave rows.
+        using S = typename EP::S;
+        constexpr bool kPair = EpiIsPaired<EP>::value;
+        constexpr int SB = (int)sizeof(S);
+        constexpr int RB = BN / EP::kDiv * SB;     // bytes per staged row
+        constexpr int CPO = RB / 16;               // 16-byte chunks per staged row
+        constexpr int XM = CPO < 16 ? CPO : 16;    // swizzle period
+        constexpr int PASSES = (BM * RB + 2 * STAGE - 1) / (2 * STAGE);
+        constexpr int WPP = WM / PASSES;           // wave rows per pass
+        constexpr int RPP = BM / PASSES;           // tile rows per pass
+        constexpr int NT = NW * 64;
+        static_assert(WM % PASSES == 0 && RB % 16 == 0 && (RPP * CPO) % NT == 0, "staging layout");
+        static_assert(!kPair || TN % 2 == 0, "paired epilogue needs an even number of column tiles per wave");
+        auto lds_at = [&](int r, int byte) {
+            return smem + r * RB + ((((byte >> 4) ^ (r & (XM - 1))) << 4) | (byte & 15));
+        };
+        constexpr int Q = RPP * CPO / NT;          // row-phase chunks per thread per band
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int p = 0; p < PASSES; ++p) {
+            uint4 pv[Q];                           // per-chunk operands of the row phase (the residual)
 #pragma unroll
-            for (int j = 0; j < TN; j += 2)
-                ep.pair(m0 + (wm * TM + i) * 16 + fr, n0 + (wn * TN + j) * 16 + 4 * fg, acc[i][j], acc[i][j + 1]);
+            for (int q = 0; q < Q; ++q) {
+                const int idx = q * NT + tid;
+                pv[q] = ep.pre(m0 + p * RPP + idx / CPO, n0 / EP::kDiv + (idx % CPO) * (16 / SB));
+            }
+            if (p) __syncthreads();                // the previous band has been read
+            if (wm / WPP == p) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; j += kPair ? 2 : 1) {
+                        const int r = (wm % WPP) * TM * 16 + i * 16 + fr;
+                        const int c = (kPair ? (wn * TN + j) / 2 : wn * TN + j) * 16 + 4 * fg;
+                        float v[4];
+                        if constexpr (kPair) ep.pair(acc[i][j], acc[i][j + 1], v);
+                        else ep.frag(acc[i][j], v);
+                        store4(reinterpret_cast<S*>(lds_at(r, c * SB)), v[0], v[1], v[2], v[3]);
+                    }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int idx = q * NT + tid, r = idx / CPO, c = idx % CPO;
+                ep.row(m0 + p * RPP + r, n0 / EP::kDiv + c * (16 / SB), ld16(lds_at(r, c * 16)), pv[q]);
+            }
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -472,7 +579,7 @@ hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win,
     if (C % kConvCB) return hipErrorInvalidValue;
     ConvA<T> al{in, M, Hin, Win, C, Hout, Wout, time_major, blocked_in ? kConvCB : C,
                 blocked_in ? Hin * Win * kConvCB : kConvCB};
-    EpiBias<T> ep{out, bias, M, C, true};
+    EpiBias<T, true> ep{out, bias, M, C};
     if (C % Elem<T>::per16) return hipErrorInvalidValue;
     return time_major ? run<kConv3>(s, al, M, w, C, 9 * C, ep) : run<kConv2>(s, al, M, w, C, 9 * C, ep);
 }
@@ -489,10 +596,9 @@ template <typename T>
 hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N, const float* bias,
                      T* out, bool gelu) {
     DenseA<T> al{a, M, K, K};
-    EpiBias<T> ep{out, bias, M, N, gelu};
-    if (!gelu) return run<kQKV>(s, al, M, w, N, K, ep);
-    if (N != K) return run<kFC1>(s, al, M, w, N, K, ep);
-    return run<kProj1>(s, al, M, w, N, K, ep);
+    if (!gelu) return run<kQKV>(s, al, M, w, N, K, EpiBias<T, false>{out, bias, M, N});
+    if (N != K) return run<kFC1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N});
+    return run<kProj1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N});
 }
 
 template <typename T>
@@ -517,7 +623,7 @@ hipError_t thinker_gemm(hipStream_t s, int site, const T* a, int M, int K, const
                         const float* zero, T* out_t, float* x) {
     DenseA<T> al{a, M, K, K};
     switch (site) {
-        case kTQKV: return run<kTQKV>(s, al, M, w, N, K, EpiBias<T>{out_t, zero, M, N, false});
+        case kTQKV: return run<kTQKV>(s, al, M, w, N, K, EpiBias<T, false>{out_t, zero, M, N});
         case kTOProj: return run<kTOProj>(s, al, M, w, N, K, EpiResid{x, zero, M, N});
         case kTDown: return run<kTDown>(s, al, M, w, N, K, EpiResid{x, zero, M, N});
         case kTGateUp:
