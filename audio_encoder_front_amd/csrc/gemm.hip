@@ -228,7 +228,7 @@ struct EpiBias {           // out = acc + bias (GELU if kGelu), stored as T
     __device__ f32x4 init(int n) const { return n < N ? load4_tail(bias, n, N) : f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ void frag(f32x4 v, float* o) const {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = kGelu ? gelu_erf(v[r]) : v[r];
+        for (int r = 0; r < 4; ++r) o[r] = kGelu ? gelu_for<T>(v[r]) : v[r];
     }
     __device__ uint4 pre(int, int) const { return zero16(); }
     __device__ void row(int m, int n, uint4 c, uint4) const {

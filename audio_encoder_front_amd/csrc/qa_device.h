@@ -38,13 +38,19 @@ __device__ __forceinline__ void mfma_kblock(float, const uint4& a, const uint4& 
 }
 
 // GELU with the erf (not tanh) form, gelu(z) = z (1 + erf(z / sqrt 2)) / 2,
-// written as relu(z) - a erfc(a / sqrt 2) / 2 with a = min(|z|, 6), and
-// erfc(a / sqrt 2) / 2 = exp2(P(a)) for a degree-6 polynomial P fitted to
+// written as relu(z) - a erfc(a / sqrt 2) / 2 with a = min(|z|, A), and
+// erfc(a / sqrt 2) / 2 = exp2(P(a)) for a polynomial P fitted to
 // log2(erfc(a / sqrt 2)) - 1, weighted by the GELU error it causes
 // (gelu_coeffs.py in this package derives and checks the coefficients).
-// Horner in fp32, one exp2: absolute error <= 2.7e-7 over the fp32 range
-// (float32 emulation against the exact erf); past |z| = 6 the tail term is
-// below 1e-8.  +inf maps to +inf, -inf to -0.
+// Horner in fp32, one exp2, relu as a median (one instruction, no NaN
+// canonicalisation).
+//   gelu_erf:      degree 6, A = 6, absolute error <= 2.7e-7 over the fp32
+//                  range (float32 emulation against the exact erf); the tail
+//                  past |z| = 6 is below 1e-8.  For results kept in fp32.
+//   gelu_erf_bf16: degree 4, A = 5, absolute error <= 6.4e-6; the tail past
+//                  |z| = 5 is below 1.5e-6.  For results rounded to bf16 at
+//                  once (two fused multiply-adds fewer per element).
+// +inf maps to +inf, -inf to -0 (gelu_erf) or -1.4e-6 (gelu_erf_bf16).
 __device__ __forceinline__ float gelu_erf(float z) {
     const float a = __builtin_amdgcn_fmed3f(fabsf(z), 0.0f, 6.0f);
     float y = 3.454265243e-05f;
@@ -54,8 +60,20 @@ __device__ __forceinline__ float gelu_erf(float z) {
     y = fmaf(y, a, -4.587250352e-01f);
     y = fmaf(y, a, -1.151216626e+00f);
     y = fmaf(y, a, -9.999914765e-01f);
-    return fmaf(-a, __builtin_amdgcn_exp2f(y), fmaxf(z, 0.0f));
+    return fmaf(-a, __builtin_amdgcn_exp2f(y), __builtin_amdgcn_fmed3f(z, 0.0f, __builtin_inff()));
 }
+__device__ __forceinline__ float gelu_erf_bf16(float z) {
+    const float a = __builtin_amdgcn_fmed3f(fabsf(z), 0.0f, 5.0f);
+    float y = 3.872423200e-03f;
+    y = fmaf(y, a, -4.409601539e-02f);
+    y = fmaf(y, a, -4.680127501e-01f);
+    y = fmaf(y, a, -1.147355437e+00f);
+    y = fmaf(y, a, -1.000486970e+00f);
+    return fmaf(-a, __builtin_amdgcn_exp2f(y), __builtin_amdgcn_fmed3f(z, 0.0f, __builtin_inff()));
+}
+// The GELU for a result stored as T.
+template <typename T> __device__ __forceinline__ float gelu_for(float z) { return gelu_erf(z); }
+template <> __device__ __forceinline__ float gelu_for<bf16>(float z) { return gelu_erf_bf16(z); }
 
 // Store 4 consecutive values (fp32 -> 16 bytes, bf16 -> 8 bytes, RNE).
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void conv1_kernel(const float* __restrict__ lo
                 for (int q = 0; q < 8; ++q) acc[q] = fmaf(w[a * 3 + bb][q], v, acc[q]);
             }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = gelu_erf(acc[q]);
+        for (int q = 0; q < 8; ++q) acc[q] = gelu_for<T>(acc[q]);
         store8(obase + ((size_t)i * kC1Wout + j) * C + c0, acc);
     }
 }
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void conv1_mfma_kernel(const float* __restrict
             const f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[2 * cb + 1]), b, z, 0, 0, 0);
             float v[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) { v[r] = gelu_erf(a0[r]); v[4 + r] = gelu_erf(a1[r]); }
+            for (int r = 0; r < 4; ++r) { v[r] = gelu_erf_bf16(a0[r]); v[4 + r] = gelu_erf_bf16(a1[r]); }
             store8(orow + cb * kPlane, v);
         }
     }
