@@ -104,17 +104,17 @@ hipError_t layernorm(hipStream_t s, const float* x, int M, int d, const float* g
 
 constexpr int kHd = 64;
 
-template <typename T> struct AttnLds;
-template <> struct AttnLds<bf16> {
-    static constexpr int qrow = 144;               // 128 B + 16 pad
-    static constexpr int vrow = 2 * kMaxWindow + 8; // bytes per V^T row (d index)
-};
-template <> struct AttnLds<float> {
-    static constexpr int qrow = 272;               // 256 B + 16 pad
-    static constexpr int vrow = 4 * kMaxWindow + 16;
+// LDS rows: K rows of the head (64 values + 16 bytes of padding) and V^T
+// rows (one per head dimension, ROWS keys + padding), for ROWS keys.
+template <typename T, int ROWS> struct AttnLds {
+    static constexpr int qrow = 64 * (int)sizeof(T) + 16;
+    static constexpr int vrow = (int)sizeof(T) * ROWS + (sizeof(T) == 2 ? 8 : 16);
 };
 
 // P.V over one 32-key step (bf16) or one 16-key tile (fp32), accumulate o[dt].
+// HALF: the step's second key tile lies past the LDS rows (an odd number of
+// key tiles); its V values are taken as zero, its probabilities are zero.
+template <int VR, bool HALF = false>
 __device__ __forceinline__ void pv_step(bf16, const char* vt, int kbase, int fr, int fg, const f32x4* p,
                                         int t0, f32x4* o) {
     // slots 0..3: keys kbase + 4g + r (tile t0), slots 4..7: kbase + 16 + 4g + r (tile t0 + 1)
@@ -123,18 +123,19 @@ __device__ __forceinline__ void pv_step(bf16, const char* vt, int kbase, int fr,
     for (int r = 0; r < 4; ++r) { pb[r] = (bf16)p[t0][r]; pb[4 + r] = (bf16)p[t0 + 1][r]; }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const char* row = vt + (dt * 16 + fr) * AttnLds<bf16>::vrow;
+        const char* row = vt + (dt * 16 + fr) * VR;
         const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 4 * fg));
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 16 + 4 * fg));
+        const uint2 hi = HALF ? make_uint2(0u, 0u) : *reinterpret_cast<const uint2*>(row + 2 * (kbase + 16 + 4 * fg));
         const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[dt], 0, 0, 0);
     }
 }
+template <int VR>
 __device__ __forceinline__ void pv_step(float, const char* vt, int kbase, int fr, int fg, const f32x4* p,
                                         int t0, f32x4* o) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const char* row = vt + (dt * 16 + fr) * AttnLds<float>::vrow;
+        const char* row = vt + (dt * 16 + fr) * VR;
         const float4 va = *reinterpret_cast<const float4*>(row + 4 * (kbase + 4 * fg));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, p[t0][0], o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, p[t0][1], o[dt], 0, 0, 0);
@@ -143,14 +144,15 @@ __device__ __forceinline__ void pv_step(float, const char* vt, int kbase, int fr
     }
 }
 
-template <typename T>
+template <typename T, int KT>
 __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qkv, const int* __restrict__ cu,
                                                         int n_heads, int d, T* __restrict__ out) {
-    constexpr int QR = AttnLds<T>::qrow, VR = AttnLds<T>::vrow;
+    constexpr int ROWS = KT * 16;                  // keys held in LDS
+    constexpr int QR = AttnLds<T, ROWS>::qrow, VR = AttnLds<T, ROWS>::vrow;
     constexpr int PER = Elem<T>::per16;
     constexpr int CPR = kHd / PER;                 // 16-byte chunks per head row
     constexpr int KBN = kHd * (int)sizeof(T) / 64; // 64-byte MFMA K blocks per head row
-    __shared__ __align__(16) char ks[kMaxWindow * QR];
+    __shared__ __align__(16) char ks[ROWS * QR];
     __shared__ __align__(16) char vts[kHd * VR];
 
     const int win = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 
     // K and V rows of this head (16 bytes per load, every load issued before
     // any LDS store); rows at or beyond n are zeros.  V is stored transposed.
-    constexpr int NCH = kMaxWindow * CPR / 256;    // 16-byte chunks per thread per matrix
+    constexpr int NCH = (ROWS * CPR + 255) / 256;  // 16-byte chunks per thread per matrix
     uint4 kv[NCH], vv[NCH];
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
@@ -191,6 +193,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     for (int q = 0; q < NCH; ++q) {
         const int idx = tid + q * 256;
         const int t = idx / CPR, c = idx % CPR;
+        if (ROWS * CPR % 256 != 0 && t >= ROWS) continue;
         st16(ks + t * QR + c * 16, kv[q]);
         const T* ve = reinterpret_cast<const T*>(&vv[q]);
 #pragma unroll
@@ -200,6 +203,10 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     __syncthreads();
 
     const float sc = 0.125f * 1.4426950408889634f; // 1/sqrt(64) * log2(e)
+    // KT key tiles of 16 hold every key of the longest window (7 for the
+    // 104-token windows); an unused 8th tile only pairs tiles into 32-key
+    // P.V steps and stays zero.
+    static_assert(KT >= 1 && KT * 16 <= kMaxWindow, "key tiles");
     for (int qt = wave; qt < nt; qt += 4) {
         f32x4 sacc[8];
 #pragma unroll
@@ -207,32 +214,37 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {   // all 8 key tiles: rows past n are zeros, masked below
+            for (int kt = 0; kt < KT; ++kt) {   // rows past n are zeros, masked below
                 const uint4 kf = ld16(ks + (kt * 16 + fr) * QR + fg * 16 + kb * 64);
                 mfma_kblock(T(), kf, qf[kb], sacc[kt]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         if (qt + 4 < nt) load_q(qt + 4, qf);       // next tile's queries, in flight during softmax and P.V
-        // sacc[kt][r] = score(key kt*16 + 4fg + r, query qt*16 + fr)
+        // sacc[kt][r] = score(key kt*16 + 4fg + r, query qt*16 + fr).  Keys
+        // at or past n exist only in the tiles that reach n (a uniform test
+        // per tile); the max is taken on the unscaled scores (sc > 0) and
+        // the scale folded into one fma per probability.
         float mx = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
+        for (int kt = 0; kt < KT; ++kt) {
+            if (kt * 16 + 16 > n) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kt * 16 + 4 * fg + r;
-                const float v = key < n ? sacc[kt][r] * sc : -INFINITY;
-                sacc[kt][r] = v;
-                mx = fmaxf(mx, v);
+                for (int r = 0; r < 4; ++r)
+                    if (kt * 16 + 4 * fg + r >= n) sacc[kt][r] = -INFINITY;
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][r]);
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float off = -mx * sc;
         float sum = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = exp2f(sacc[kt][r] - mx);
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sc, off));
                 sacc[kt][r] = p;
                 sum += p;
             }
@@ -243,14 +255,15 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
         for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (sizeof(T) == 2) {
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {   // keys past n have p = 0 and zero V rows
-                pv_step(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+            for (int st = 0; st < (KT + 1) / 2; ++st) {   // keys past n have p = 0 and zero V rows
+                if (2 * st + 1 < KT) pv_step<VR>(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+                else pv_step<VR, true>(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
-                pv_step(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
+            for (int kt = 0; kt < KT; ++kt) {
+                pv_step<VR>(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 template <typename T>
 __global__ __launch_bounds__(256) void attention_long_kernel(const T* __restrict__ qkv, const int* __restrict__ cu,
                                                              int n_heads, int d, int qgroups, T* __restrict__ out) {
-    constexpr int QR = AttnLds<T>::qrow, VR = AttnLds<T>::vrow;
+    constexpr int QR = AttnLds<T, kMaxWindow>::qrow, VR = AttnLds<T, kMaxWindow>::vrow;
     constexpr int PER = Elem<T>::per16;
     constexpr int CPR = kHd / PER;
     constexpr int KBN = kHd * (int)sizeof(T) / 64;
@@ -374,13 +387,13 @@ __global__ __launch_bounds__(256) void attention_long_kernel(const T* __restrict
         if (sizeof(T) == 2) {
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                pv_step(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+                pv_step<VR>(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt) {
-                pv_step(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
+                pv_step<VR>(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -399,8 +412,10 @@ template <typename T>
 hipError_t attention(hipStream_t s, const T* qkv, const int* cu_seqlens, int n_windows, int n_heads,
                      int d, int max_len, T* out) {
     if (n_windows <= 0) return hipSuccess;
-    if (max_len <= kMaxWindow) {
-        attention_kernel<T><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);
+    if (max_len <= 112) {          // every window fits 7 key tiles (104-token windows)
+        attention_kernel<T, 7><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);
+    } else if (max_len <= kMaxWindow) {
+        attention_kernel<T, kMaxWindow / 16><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);
     } else {
         const int qgroups = (max_len + 63) / 64;
         attention_long_kernel<T><<<n_windows * n_heads * qgroups, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d,
