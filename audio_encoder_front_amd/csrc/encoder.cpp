@@ -78,6 +78,23 @@ float bf16_bits_to_f32(uint16_t b) {
     return f;
 }
 
+uint16_t f32_to_bf16_rne(float f) {   // finite inputs
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// v = hi + mid + lo exactly (each part a bf16; 3 x 8 significant bits cover
+// fp32's 24): hi = rne(v), mid = rne(v - hi), lo = v - hi - mid.
+void split3_bf16(float v, uint16_t* part) {
+    part[0] = f32_to_bf16_rne(v);
+    const float r1 = v - bf16_bits_to_f32(part[0]);
+    part[1] = f32_to_bf16_rne(r1);
+    const float r2 = r1 - bf16_bits_to_f32(part[1]);
+    part[2] = f32_to_bf16_rne(r2);
+}
+
 // ---------------------------------------------------------------- front-end constants
 
 double hz_to_mel(double f) {   // Slaney: linear below 1 kHz, 27 mels per factor 6.4 above
@@ -88,7 +105,7 @@ double mel_to_hz(double m) {
 }
 
 struct FrontConsts {
-    std::vector<float> basis;   // [13][100][2][4][16]
+    std::vector<uint16_t> basis;   // bf16 A fragments [13][13][2][3][64][8] (see qa::frontend)
     std::vector<float> fbB;     // [13][4][8][4][16]
     std::vector<int> range;     // [13][2]
 };
@@ -108,19 +125,26 @@ FrontConsts make_front_consts() {
             fb[(size_t)m * kBins + k] = v * 2.0 / (hi - lo);
         }
     }
-    // periodic Hann folded into the cos / sin basis; trig in fp64
-    c.basis.assign((size_t)qa::kBinChunks * 100 * 128, 0.f);
+    // periodic Hann folded into the cos / sin basis (trig in fp64, rounded to
+    // fp32), each fp32 value split exactly into bf16 hi + mid + lo and laid out
+    // as MFMA A fragments: lane l holds bin 16 bc + l % 16, samples
+    // 32 kb + 8 (l / 16) .. + 7
+    c.basis.assign((size_t)qa::kBinChunks * qa::kDftKBlocks * 2 * 3 * 64 * 8, 0);
     for (int bc = 0; bc < qa::kBinChunks; ++bc)
-        for (int kk = 0; kk < 100; ++kk)
-            for (int g = 0; g < 4; ++g)
-                for (int li = 0; li < 16; ++li) {
-                    const int bin = bc * 16 + li, n = 4 * kk + g;
-                    if (bin >= kBins) continue;
+        for (int kb = 0; kb < qa::kDftKBlocks; ++kb)
+            for (int l = 0; l < 64; ++l)
+                for (int e = 0; e < 8; ++e) {
+                    const int bin = bc * 16 + l % 16, n = 32 * kb + 8 * (l / 16) + e;
+                    if (bin >= kBins || n >= kNfft) continue;
                     const double w = 0.5 - 0.5 * std::cos(2.0 * M_PI * n / kNfft);
                     const double ang = 2.0 * M_PI * (double)((bin * n) % kNfft) / kNfft;
-                    const size_t base = (((size_t)bc * 100 + kk) * 2) * 64 + g * 16 + li;
-                    c.basis[base] = (float)(w * std::cos(ang));
-                    c.basis[base + 64] = (float)(w * std::sin(ang));
+                    const float v[2] = {(float)(w * std::cos(ang)), (float)(w * std::sin(ang))};
+                    for (int cs = 0; cs < 2; ++cs) {
+                        uint16_t part[3];
+                        split3_bf16(v[cs], part);
+                        for (int pp = 0; pp < 3; ++pp)
+                            c.basis[(((((size_t)bc * qa::kDftKBlocks + kb) * 2 + cs) * 3 + pp) * 64 + l) * 8 + e] = part[pp];
+                    }
                 }
     c.fbB.assign((size_t)qa::kBinChunks * 4 * 8 * 64, 0.f);
     c.range.assign(2 * qa::kBinChunks, 0);
@@ -424,7 +448,7 @@ QA_API qa_encoder* qa_encoder_create(const qa_weights* w, const qa_dims* d) {
     e->proj2_w = put_op(f32vec(w->proj2_w, (size_t)O * D));
     e->proj2_b = put_f32(f32vec(w->proj2_b, O));
     FrontConsts fc = make_front_consts();
-    e->basis = put_f32(fc.basis);
+    e->basis = pk.put(fc.basis.data(), fc.basis.size() * sizeof(uint16_t));
     e->fbB = put_f32(fc.fbB);
     e->fb_range = pk.put(fc.range.data(), fc.range.size() * sizeof(int));
     e->pe = put_f32(make_pe(D));
@@ -662,7 +686,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
 
     QA_LAUNCH("tables", hipMemcpyAsync(ws, e->pinned, table_bytes, hipMemcpyHostToDevice, s));
     QA_LAUNCH("init", qa::init_flags(s, key, n_clips, flag));
-    QA_LAUNCH("frontend", qa::frontend(s, pcm, d_clips, d_tiles, n_tiles, e->W<float>(e->basis), e->W<float>(e->fbB),
+    QA_LAUNCH("frontend", qa::frontend(s, pcm, d_clips, d_tiles, n_tiles, e->W<uint4>(e->basis), e->W<float>(e->fbB),
                                        e->W<int>(e->fb_range), logmel, key, flag));
     QA_LAUNCH("normalize", qa::normalize(s, logmel, d_clips, d_tiles, n_tiles, key));
     if constexpr (std::is_same<T, qa::bf16>::value) {

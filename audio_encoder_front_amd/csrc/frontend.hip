@@ -1,4 +1,4 @@
-// Front end: framing + periodic-Hann 400-point real DFT as an fp32 MFMA GEMM,
+// Front end: framing + periodic-Hann 400-point real DFT as an MFMA GEMM,
 // power spectrum, 128-filter Slaney mel GEMM, 1e-10 floor, log10 and the
 // per-clip maximum; then the peak-minus-8 clip and (x+4)/4 affine.
 //
@@ -8,29 +8,38 @@
 // reflection, Slaney mel, power floor 1e-10, log10 peak-minus-eight, (x+4)/4,
 // floor(len/160) frames).
 //
-// Kernel design (two waves per 64-frame tile, splitting the DFT bins):
-//  * the tile's samples (with mirror padding) sit in LDS, two pad words every
-//    160 samples so that the 16 frames x 4 samples a fragment reads fall in
-//    distinct banks;
-//  * GEMM 1 is computed transposed, D[bin][frame] = sum_n basis[n][bin] x[frame][n],
-//    with the Hann window folded into the basis; for each block of 16 bins the
-//    cos and sin products land in matching registers, so the power needs no
-//    data movement;
-//  * the lane layout of D is exactly the A-operand layout GEMM 2 needs
-//    (frame = lane%16, bin = 4*(lane/16) + r at k-step r), so the power feeds
-//    the mel MFMA straight from registers;
-//  * mel tiles with no nonzero filter weight for a bin block are skipped;
-//  * the two waves take alternate 16-bin blocks; their partial mel energies
-//    meet in LDS (the sample buffer is free by then) before the log.
+// Kernel design (four waves per 64-frame tile):
+//  * the DFT runs on the bf16 MFMA at fp32 accuracy: every fp32 sample and
+//    every fp32 basis value (Hann window folded in) is split exactly into
+//    three bf16 parts, hi + mid + lo, and each product keeps the six part
+//    products whose exponents reach the fp32 result (hi.hi, hi.mid, mid.hi,
+//    hi.lo, mid.mid, lo.hi); the three dropped ones are below 2^-24 of it.
+//    Six 16x16x32 bf16 MFMAs replace eight 16x16x4 fp32 ones per 32 samples
+//    (96 instead of 256 MFMA cycles);
+//  * the tile's samples, split, sit in LDS as three bf16 planes with 8 pad
+//    samples after every 160, so the 16 frames x 8 samples a fragment reads
+//    hit 16 distinct 4-bank groups;
+//  * D[bin][frame] = sum_n basis[n][bin] x[frame][n]: wave w takes the
+//    16-bin chunks w, w + 4, w + 8, w + 12 for all 64 frames (cos and sin of
+//    a bin in the same registers, so the power needs no data movement), the
+//    basis fragments come pre-split and pre-laid-out from global memory;
+//  * the power goes to LDS bin-major (the sample planes are free by then),
+//    and wave w computes the mel energies of frames 16 w .. 16 w + 15 on the
+//    fp32 MFMA, skipping mel tiles with no nonzero filter weight for a bin
+//    chunk; then log10, the clip maximum and the store.
 #include "qa_device.h"
 #include "qa_kernels.h"
 
 namespace qa {
 
-constexpr int kSpan = 160 * (kFrontFrames - 1) + 400;          // samples per tile
-constexpr int kLdsSamples = kSpan + 2 * (kSpan / 160) + 4;
+constexpr int kDftKB = 13;                                     // 32-sample K blocks (416 >= 400)
+constexpr int kSpan = 160 * (kFrontFrames - 1) + 32 * kDftKB;  // samples a tile reads (K padded)
+constexpr int kPlane = kSpan + 8 * (kSpan / 160) + 8;          // padded bf16 samples per plane
+constexpr int kPStride = 4 * kFrontFrames / 4 + 4;             // floats per power row (one bin): 68
+constexpr int kFrontLds = 3 * kPlane * 2 > kBinChunks * 16 * kPStride * 4 ? 3 * kPlane * 2
+                                                                           : kBinChunks * 16 * kPStride * 4;
 
-__device__ __forceinline__ int pad_index(int s) { return s + 2 * (s / 160); }
+__device__ __forceinline__ int pad_index(int s) { return s + 8 * (s / 160); }
 
 __global__ void init_flags_kernel(int* clip_key, int n_clips, int* flag) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -38,12 +47,14 @@ __global__ void init_flags_kernel(int* clip_key, int n_clips, int* flag) {
     if (i == 0) *flag = 0;
 }
 
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void frontend_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void frontend_kernel(
     const float* __restrict__ pcm, const ClipInfo* __restrict__ clips,
-    const FrontTile* __restrict__ tiles, const float* __restrict__ basis,
+    const FrontTile* __restrict__ tiles, const uint4* __restrict__ basis,
     const float* __restrict__ fbB, const int* __restrict__ fb_range,
     float* __restrict__ logmel, int* __restrict__ clip_key, int* __restrict__ flag) {
-    __shared__ float xs[kLdsSamples];
+    __shared__ __align__(16) char lds[kFrontLds];
+    bf16* planes = reinterpret_cast<bf16*>(lds);          // [3][kPlane]
+    float* pw = reinterpret_cast<float*>(lds);            // [208 bins][kPStride], after the DFT
     const FrontTile t = tiles[blockIdx.x];
     const ClipInfo c = clips[t.clip];
     const float* x = pcm + c.sample_off;
@@ -51,107 +62,158 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void f
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nsamp = 160 * (t.nframes - 1) + 400;
     bool bad = false;
-    for (int s = threadIdx.x; s < kSpan; s += 128) {
-        float v = 0.0f;
-        if (s < nsamp) {
-            int i = 160 * t.frame0 + s - 200;     // centered: frame j starts 200 samples early
-            if (i < 0) i = -i;                      // mirror without repeating the edge
-            if (i >= L) i = 2 * (L - 1) - i;
-            v = x[i];
-            bad |= !isfinite(v);
+    // Samples in pairs (a pair never straddles a pad): every load of the tile
+    // is issued before the first split, then each part plane gets one
+    // 4-byte write per pair.
+    constexpr int NP = (kSpan / 2 + 255) / 256;
+    float va[NP], vb[NP];
+    auto sample = [&](int s) {
+        if (s >= nsamp) return 0.0f;
+        int i = 160 * t.frame0 + s - 200;         // centered: frame j starts 200 samples early
+        if (i < 0) i = -i;                          // mirror without repeating the edge
+        if (i >= L) i = 2 * (L - 1) - i;
+        return x[i];
+    };
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        const int s = 2 * ((int)threadIdx.x + 256 * k);
+        va[k] = s < kSpan ? sample(s) : 0.0f;
+        vb[k] = s < kSpan ? sample(s + 1) : 0.0f;
+    }
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        const int s = 2 * ((int)threadIdx.x + 256 * k);
+        if (s >= kSpan) continue;
+        float v[2] = {va[k], vb[k]};
+        bf16x2 part[3];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            bad |= !isfinite(v[e]);
+            if (!isfinite(v[e])) v[e] = 0.0f;       // reported through the flag; keep the MFMA finite
+            const bf16 hi = (bf16)v[e];
+            const float r1 = v[e] - (float)hi;
+            const bf16 mid = (bf16)r1;
+            part[0][e] = hi;
+            part[1][e] = mid;
+            part[2][e] = (bf16)(r1 - (float)mid);
         }
-        xs[pad_index(s)] = v;
+        const int q = pad_index(s);
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) *reinterpret_cast<bf16x2*>(planes + pp * kPlane + q) = part[pp];
     }
     __syncthreads();
 
     const int g = lane >> 4, li = lane & 15;
-    f32x4 E[4][8];
+    // acc[slot][cs][ft]: bins 16 bc + 4 g + r, bc = wave + 4 slot, of frame 16 ft + li (cs: cos, sin)
+    f32x4 acc[4][2][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) E[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    int fbase[4];
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft) fbase[ft] = 162 * (ft * 16 + li);   // pad_index(160*frame)
-
-    for (int bc = wave; bc < kBinChunks; bc += 2) {
-        f32x4 re[4], im[4];
+            for (int f = 0; f < 4; ++f) acc[a][b][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // (K block, chunk slot) units of this wave in order; the basis fragments
+    // of the next unit are loaded while the current one multiplies.
+    const int nslots = (kBinChunks - wave + 3) / 4;   // 4 for wave 0, 3 for the others
+    const int nunits = kDftKB * nslots;
+    auto load_basis = [&](int u, uint4* b) {
+        const int kb = u / nslots, bc = wave + 4 * (u % nslots);
+        const uint4* bp = basis + (size_t)((bc * kDftKB + kb) * 2) * 3 * 64 + lane;
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) { re[ft] = f32x4{0.f, 0.f, 0.f, 0.f}; im[ft] = re[ft]; }
-        const float* bp = basis + (size_t)bc * 100 * 128 + g * 16 + li;
-#pragma unroll 4
-        for (int kk = 0; kk < 100; ++kk) {
-            const float bcos = bp[kk * 128];
-            const float bsin = bp[kk * 128 + 64];
-            const int n = 4 * kk + g;
-            const int off = n + 2 * (n / 160);
+        for (int q = 0; q < 6; ++q) b[q] = bp[q * 64];   // cos hi, mid, lo, sin hi, mid, lo
+    };
+    uint4 bcur[6], bnxt[6];
+    load_basis(0, bcur);
+    bf16x8 xf[4][3];
+    for (int u = 0; u < nunits; ++u) {
+        const int kb = u / nslots, slot = u % nslots;
+        if (u + 1 < nunits) load_basis(u + 1, bnxt);
+        if (slot == 0) {
+            // B operand: 8 consecutive samples 32 kb + 8 g .. of frame 16 ft + li, per part
 #pragma unroll
             for (int ft = 0; ft < 4; ++ft) {
-                const float xv = xs[fbase[ft] + off];
-                re[ft] = __builtin_amdgcn_mfma_f32_16x16x4f32(bcos, xv, re[ft], 0, 0, 0);
-                im[ft] = __builtin_amdgcn_mfma_f32_16x16x4f32(bsin, xv, im[ft], 0, 0, 0);
+                const int q = pad_index(160 * (16 * ft + li) + 32 * kb + 8 * g);
+#pragma unroll
+                for (int p = 0; p < 3; ++p) xf[ft][p] = __builtin_bit_cast(bf16x8, ld16(planes + p * kPlane + q));
             }
         }
-        // power P[bin 4g+r][frame ft*16+li] = re^2 + im^2 (no sqrt)
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) re[ft] = re[ft] * re[ft] + im[ft] * im[ft];
-        const int lo = fb_range[2 * bc], hi = fb_range[2 * bc + 1];
+        for (int sl = 0; sl < 4; ++sl) {
+            if (sl != slot) continue;                 // register-indexed accumulators stay static
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            if (mt < lo || mt >= hi) continue;      // wave-uniform: all-zero filter tile
+            for (int cs = 0; cs < 2; ++cs) {
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, bcur[3 * cs]);
+                const bf16x8 bm = __builtin_bit_cast(bf16x8, bcur[3 * cs + 1]);
+                const bf16x8 bl = __builtin_bit_cast(bf16x8, bcur[3 * cs + 2]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float fb = fbB[(((size_t)bc * 4 + r) * 8 + mt) * 64 + lane];
-#pragma unroll
-                for (int ft = 0; ft < 4; ++ft)
-                    E[ft][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(re[ft][r], fb, E[ft][mt], 0, 0, 0);
-            }
-        }
-    }
-
-    // combine the two waves' partial mel energies through LDS
-    __syncthreads();
-    float4* ex = reinterpret_cast<float4*>(xs);
-    if (wave == 1) {
-#pragma unroll
-        for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-                ex[(ft * 8 + mt) * 64 + lane] = make_float4(E[ft][mt][0], E[ft][mt][1], E[ft][mt][2], E[ft][mt][3]);
-    }
-    __syncthreads();
-    if (wave == 1) {
-        if (__any(bad) && lane == 0) atomicOr(flag, 1);
-        return;
-    }
-#pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const float4 o = ex[(ft * 8 + mt) * 64 + lane];
-            E[ft][mt][0] += o.x; E[ft][mt][1] += o.y; E[ft][mt][2] += o.z; E[ft][mt][3] += o.w;
-        }
-
-    // E[ft][mt] lane holds mel energy of frame ft*16 + 4g + r, mel mt*16 + li.
-    float vmax = -INFINITY;
-    float* outp = logmel + (size_t)(c.frame_row0 + t.frame0) * kMels;
-#pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int fi = ft * 16 + 4 * g + r;
-            if (fi < t.nframes) {
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt) {
-                    const float e = E[ft][mt][r];
-                    bad |= !isfinite(e);             // power beyond float32 range
-                    const float lg = log10f(fmaxf(e, 1e-10f));
-                    outp[(size_t)fi * kMels + mt * 16 + li] = lg;
-                    vmax = fmaxf(vmax, lg);
+                for (int ft = 0; ft < 4; ++ft) {
+                    f32x4 a = acc[sl][cs][ft];
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, xf[ft][0], a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bm, xf[ft][1], a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, xf[ft][2], a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bm, xf[ft][0], a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, xf[ft][1], a, 0, 0, 0);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, xf[ft][0], a, 0, 0, 0);
+                    acc[sl][cs][ft] = a;
                 }
             }
         }
+#pragma unroll
+        for (int q = 0; q < 6; ++q) bcur[q] = bnxt[q];
+    }
+    __syncthreads();                                  // every wave is done with the sample planes
+
+    // power P[bin][frame] = re^2 + im^2 (no sqrt), bin-major in LDS: the
+    // mel MFMA below reads 16 frames x 4 bins (bins 4 apart) per k-step
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+        const int bc = wave + 4 * slot;
+        if (bc >= kBinChunks) continue;
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float re = acc[slot][0][ft][r], im = acc[slot][1][ft][r];
+                pw[(16 * bc + 4 * g + r) * kPStride + 16 * ft + li] = re * re + im * im;
+            }
+    }
+    __syncthreads();
+
+    // mel energies of frames 16 wave .. + 15: E[mt] lane holds frame 16 wave + 4 g + r, mel 16 mt + li
+    f32x4 E[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) E[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bc = 0; bc < kBinChunks; ++bc) {
+        const int lo = fb_range[2 * bc], hi = fb_range[2 * bc + 1];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pv = pw[(16 * bc + 4 * g + r) * kPStride + 16 * wave + li];
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                if (mt < lo || mt >= hi) continue;      // wave-uniform: all-zero filter tile
+                const float fb = fbB[(((size_t)bc * 4 + r) * 8 + mt) * 64 + lane];
+                E[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, fb, E[mt], 0, 0, 0);
+            }
+        }
+    }
+
+    float vmax = -INFINITY;
+    float* outp = logmel + (size_t)(c.frame_row0 + t.frame0) * kMels;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int fi = 16 * wave + 4 * g + r;
+        if (fi < t.nframes) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const float e = E[mt][r];
+                bad |= !isfinite(e);                 // power beyond float32 range
+                const float lg = log10f(fmaxf(e, 1e-10f));
+                outp[(size_t)fi * kMels + mt * 16 + li] = lg;
+                vmax = fmaxf(vmax, lg);
+            }
+        }
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o));
     if (lane == 0) atomicMax(clip_key + t.clip, float_key(vmax));
@@ -184,10 +246,10 @@ hipError_t init_flags(hipStream_t s, int* clip_key, int n_clips, int* flag) {
 }
 
 hipError_t frontend(hipStream_t s, const float* pcm, const ClipInfo* clips, const FrontTile* tiles,
-                    int n_tiles, const float* basis, const float* fbB, const int* fb_range,
+                    int n_tiles, const uint4* basis, const float* fbB, const int* fb_range,
                     float* logmel, int* clip_key, int* flag) {
     if (n_tiles <= 0) return hipSuccess;
-    frontend_kernel<<<n_tiles, 128, 0, s>>>(pcm, clips, tiles, basis, fbB, fb_range, logmel, clip_key, flag);
+    frontend_kernel<<<n_tiles, 256, 0, s>>>(pcm, clips, tiles, basis, fbB, fb_range, logmel, clip_key, flag);
     return hipGetLastError();
 }
 

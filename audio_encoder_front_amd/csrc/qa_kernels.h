@@ -44,8 +44,14 @@ void set_error_message(const char* msg);
 
 // ---- front end
 hipError_t init_flags(hipStream_t s, int* clip_key, int n_clips, int* flag);
+// basis: the Hann-windowed cos / sin DFT basis as bf16 MFMA A fragments, each
+// fp32 value split exactly into hi + mid + lo: [13 bin chunks][13 K blocks of
+// 32 samples][cos, sin][hi, mid, lo][64 lanes] x 8 bf16 (lane l: bin
+// 16 chunk + l % 16, samples 32 kb + 8 (l / 16) .. + 7; zero past bin 200 and
+// sample 399).
+constexpr int kDftKBlocks = 13;
 hipError_t frontend(hipStream_t s, const float* pcm, const ClipInfo* clips, const FrontTile* tiles,
-                    int n_tiles, const float* basis, const float* fbB, const int* fb_range,
+                    int n_tiles, const uint4* basis, const float* fbB, const int* fb_range,
                     float* logmel, int* clip_key, int* flag);
 hipError_t normalize(hipStream_t s, float* logmel, const ClipInfo* clips, const FrontTile* tiles,
                      int n_tiles, const int* clip_key);
