@@ -106,8 +106,9 @@ double mel_to_hz(double m) {
 
 struct FrontConsts {
     std::vector<uint16_t> basis;   // bf16 A fragments [13][13][2][3][64][8] (see qa::frontend)
-    std::vector<float> fbB;     // [13][4][8][4][16]
-    std::vector<int> range;     // [13][2]
+    std::vector<float> melw;    // [128][qa::kMelTaps] weights of bins melb0[m] ..
+    std::vector<int> melb0;     // [128] first bin of each band
+    bool ok = true;             // every band fits qa::kMelTaps bins
 };
 
 FrontConsts make_front_consts() {
@@ -146,22 +147,21 @@ FrontConsts make_front_consts() {
                             c.basis[(((((size_t)bc * qa::kDftKBlocks + kb) * 2 + cs) * 3 + pp) * 64 + l) * 8 + e] = part[pp];
                     }
                 }
-    c.fbB.assign((size_t)qa::kBinChunks * 4 * 8 * 64, 0.f);
-    c.range.assign(2 * qa::kBinChunks, 0);
-    for (int bc = 0; bc < qa::kBinChunks; ++bc) {
-        int lo = 8, hi = 0;
-        for (int r = 0; r < 4; ++r)
-            for (int mt = 0; mt < 8; ++mt)
-                for (int g = 0; g < 4; ++g)
-                    for (int li = 0; li < 16; ++li) {
-                        const int bin = bc * 16 + 4 * g + r, mel = mt * 16 + li;
-                        const double v = bin < kBins ? fb[(size_t)mel * kBins + bin] : 0.0;
-                        c.fbB[((((size_t)bc * 4 + r) * 8 + mt) * 4 + g) * 16 + li] = (float)v;
-                        if (v != 0.0) { lo = std::min(lo, mt); hi = std::max(hi, mt + 1); }
-                    }
-        if (hi <= lo) lo = hi = 0;
-        c.range[2 * bc] = lo;
-        c.range[2 * bc + 1] = hi;
+    // each band's support (consecutive bins) in a kMelTaps-wide window
+    c.melw.assign((size_t)qa::kMels * qa::kMelTaps, 0.f);
+    c.melb0.assign(qa::kMels, 0);
+    for (int m = 0; m < qa::kMels; ++m) {
+        int lo = kBins, hi = -1;
+        for (int k = 0; k < kBins; ++k)
+            if (fb[(size_t)m * kBins + k] != 0.0) { lo = std::min(lo, k); hi = std::max(hi, k); }
+        if (hi < lo) lo = hi = 0;
+        if (hi - lo + 1 > qa::kMelTaps) c.ok = false;
+        const int b0 = std::min(lo, qa::kBinChunks * 16 - qa::kMelTaps);
+        c.melb0[m] = b0;
+        for (int j = 0; j < qa::kMelTaps; ++j) {
+            const int k = b0 + j;
+            c.melw[(size_t)m * qa::kMelTaps + j] = k < kBins ? (float)fb[(size_t)m * kBins + k] : 0.f;
+        }
     }
     return c;
 }
@@ -202,7 +202,7 @@ struct qa_encoder {
     size_t conv1_w = 0, conv1_b = 0, conv2_w = 0, conv2_b = 0, conv3_w = 0, conv3_b = 0, conv_out_w = 0;
     std::vector<LayerW> layers;
     size_t post_ln_w = 0, post_ln_b = 0, proj1_w = 0, proj1_b = 0, proj2_w = 0, proj2_b = 0;
-    size_t basis = 0, fbB = 0, fb_range = 0, pe = 0;
+    size_t basis = 0, melw = 0, melb0 = 0, pe = 0;
     // per-call workspace
     char* ws = nullptr;
     size_t ws_size = 0;
@@ -448,9 +448,14 @@ QA_API qa_encoder* qa_encoder_create(const qa_weights* w, const qa_dims* d) {
     e->proj2_w = put_op(f32vec(w->proj2_w, (size_t)O * D));
     e->proj2_b = put_f32(f32vec(w->proj2_b, O));
     FrontConsts fc = make_front_consts();
+    if (!fc.ok) {   // a mel band wider than the kernel's tap window: a build defect, not an input error
+        set_err("internal: mel filter support exceeds the front-end tap window");
+        delete e;
+        return nullptr;
+    }
     e->basis = pk.put(fc.basis.data(), fc.basis.size() * sizeof(uint16_t));
-    e->fbB = put_f32(fc.fbB);
-    e->fb_range = pk.put(fc.range.data(), fc.range.size() * sizeof(int));
+    e->melw = put_f32(fc.melw);
+    e->melb0 = pk.put(fc.melb0.data(), fc.melb0.size() * sizeof(int));
     e->pe = put_f32(make_pe(D));
 
     hipError_t st = hipGetDevice(&e->device);
@@ -686,8 +691,8 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
 
     QA_LAUNCH("tables", hipMemcpyAsync(ws, e->pinned, table_bytes, hipMemcpyHostToDevice, s));
     QA_LAUNCH("init", qa::init_flags(s, key, n_clips, flag));
-    QA_LAUNCH("frontend", qa::frontend(s, pcm, d_clips, d_tiles, n_tiles, e->W<uint4>(e->basis), e->W<float>(e->fbB),
-                                       e->W<int>(e->fb_range), logmel, key, flag));
+    QA_LAUNCH("frontend", qa::frontend(s, pcm, d_clips, d_tiles, n_tiles, e->W<uint4>(e->basis), e->W<float>(e->melw),
+                                       e->W<int>(e->melb0), logmel, key, flag));
     QA_LAUNCH("normalize", qa::normalize(s, logmel, d_clips, d_tiles, n_tiles, key));
     if constexpr (std::is_same<T, qa::bf16>::value) {
         if (e->conv1_frag)

@@ -23,10 +23,12 @@
 //    16-bin chunks w, w + 4, w + 8, w + 12 for all 64 frames (cos and sin of
 //    a bin in the same registers, so the power needs no data movement), the
 //    basis fragments come pre-split and pre-laid-out from global memory;
-//  * the power goes to LDS bin-major (the sample planes are free by then),
-//    and wave w computes the mel energies of frames 16 w .. 16 w + 15 on the
-//    fp32 MFMA, skipping mel tiles with no nonzero filter weight for a bin
-//    chunk; then log10, the clip maximum and the store.
+//  * the power goes to LDS frame-major (the sample planes are free by then);
+//    a Slaney filter covers at most 9 consecutive bins, so each thread sums
+//    one mel band of 32 frames directly (kMelTaps weights in registers, fp32
+//    FMAs): 402 multiply-adds per frame instead of a mostly-zero dense GEMM;
+//    then log10, the clip maximum and the store (a workgroup writes whole
+//    512-byte log-mel rows).
 #include "qa_device.h"
 #include "qa_kernels.h"
 
@@ -35,9 +37,8 @@ namespace qa {
 constexpr int kDftKB = 13;                                     // 32-sample K blocks (416 >= 400)
 constexpr int kSpan = 160 * (kFrontFrames - 1) + 32 * kDftKB;  // samples a tile reads (K padded)
 constexpr int kPlane = kSpan + 8 * (kSpan / 160) + 8;          // padded bf16 samples per plane
-constexpr int kPStride = 4 * kFrontFrames / 4 + 4;             // floats per power row (one bin): 68
-constexpr int kFrontLds = 3 * kPlane * 2 > kBinChunks * 16 * kPStride * 4 ? 3 * kPlane * 2
-                                                                           : kBinChunks * 16 * kPStride * 4;
+constexpr int kPStride = kBinChunks * 16 + 4;                  // floats per power row (one frame): 212
+constexpr int kFrontLds = 3 * kPlane * 2 > kFrontFrames * kPStride * 4 ? 3 * kPlane * 2 : kFrontFrames * kPStride * 4;
 
 __device__ __forceinline__ int pad_index(int s) { return s + 8 * (s / 160); }
 
@@ -50,11 +51,11 @@ __global__ void init_flags_kernel(int* clip_key, int n_clips, int* flag) {
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void frontend_kernel(
     const float* __restrict__ pcm, const ClipInfo* __restrict__ clips,
     const FrontTile* __restrict__ tiles, const uint4* __restrict__ basis,
-    const float* __restrict__ fbB, const int* __restrict__ fb_range,
+    const float* __restrict__ melw, const int* __restrict__ melb0,
     float* __restrict__ logmel, int* __restrict__ clip_key, int* __restrict__ flag) {
     __shared__ __align__(16) char lds[kFrontLds];
     bf16* planes = reinterpret_cast<bf16*>(lds);          // [3][kPlane]
-    float* pw = reinterpret_cast<float*>(lds);            // [208 bins][kPStride], after the DFT
+    float* pw = reinterpret_cast<float*>(lds);            // [64 frames][kPStride], after the DFT
     const FrontTile t = tiles[blockIdx.x];
     const ClipInfo c = clips[t.clip];
     const float* x = pcm + c.sample_off;
@@ -164,55 +165,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     }
     __syncthreads();                                  // every wave is done with the sample planes
 
-    // power P[bin][frame] = re^2 + im^2 (no sqrt), bin-major in LDS: the
-    // mel MFMA below reads 16 frames x 4 bins (bins 4 apart) per k-step
+    // power P[frame][bin] = re^2 + im^2 (no sqrt): a lane's four bins of a
+    // frame are consecutive, one 16-byte write
 #pragma unroll
     for (int slot = 0; slot < 4; ++slot) {
         const int bc = wave + 4 * slot;
         if (bc >= kBinChunks) continue;
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft)
+        for (int ft = 0; ft < 4; ++ft) {
+            f32x4 pwr;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float re = acc[slot][0][ft][r], im = acc[slot][1][ft][r];
-                pw[(16 * bc + 4 * g + r) * kPStride + 16 * ft + li] = re * re + im * im;
+                pwr[r] = re * re + im * im;
             }
+            *reinterpret_cast<f32x4*>(pw + (16 * ft + li) * kPStride + 16 * bc + 4 * g) = pwr;
+        }
     }
     __syncthreads();
 
-    // mel energies of frames 16 wave .. + 15: E[mt] lane holds frame 16 wave + 4 g + r, mel 16 mt + li
-    f32x4 E[8];
+    // mel band m of frames fo, fo + 2, ..: E = sum_j w[j] P[frame][b0 + j]
+    const int m = threadIdx.x & (kMels - 1), fo = threadIdx.x / kMels;
+    const int b0 = melb0[m];
+    float w[kMelTaps];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) E[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int bc = 0; bc < kBinChunks; ++bc) {
-        const int lo = fb_range[2 * bc], hi = fb_range[2 * bc + 1];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pv = pw[(16 * bc + 4 * g + r) * kPStride + 16 * wave + li];
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                if (mt < lo || mt >= hi) continue;      // wave-uniform: all-zero filter tile
-                const float fb = fbB[(((size_t)bc * 4 + r) * 8 + mt) * 64 + lane];
-                E[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, fb, E[mt], 0, 0, 0);
-            }
-        }
-    }
-
+    for (int j = 0; j < kMelTaps; ++j) w[j] = melw[m * kMelTaps + j];
     float vmax = -INFINITY;
-    float* outp = logmel + (size_t)(c.frame_row0 + t.frame0) * kMels;
+    float* outp = logmel + (size_t)(c.frame_row0 + t.frame0) * kMels + m;
+    for (int f = fo; f < t.nframes; f += 256 / kMels) {
+        const float* pr = pw + f * kPStride + b0;
+        float e = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int fi = 16 * wave + 4 * g + r;
-        if (fi < t.nframes) {
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const float e = E[mt][r];
-                bad |= !isfinite(e);                 // power beyond float32 range
-                const float lg = log10f(fmaxf(e, 1e-10f));
-                outp[(size_t)fi * kMels + mt * 16 + li] = lg;
-                vmax = fmaxf(vmax, lg);
-            }
-        }
+        for (int j = 0; j < kMelTaps; ++j) e = fmaf(w[j], pr[j], e);
+        bad |= !isfinite(e);                     // power beyond float32 range
+        const float lg = log10f(fmaxf(e, 1e-10f));
+        outp[(size_t)f * kMels] = lg;
+        vmax = fmaxf(vmax, lg);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o));
@@ -246,10 +234,10 @@ hipError_t init_flags(hipStream_t s, int* clip_key, int n_clips, int* flag) {
 }
 
 hipError_t frontend(hipStream_t s, const float* pcm, const ClipInfo* clips, const FrontTile* tiles,
-                    int n_tiles, const uint4* basis, const float* fbB, const int* fb_range,
+                    int n_tiles, const uint4* basis, const float* melw, const int* melb0,
                     float* logmel, int* clip_key, int* flag) {
     if (n_tiles <= 0) return hipSuccess;
-    frontend_kernel<<<n_tiles, 256, 0, s>>>(pcm, clips, tiles, basis, fbB, fb_range, logmel, clip_key, flag);
+    frontend_kernel<<<n_tiles, 256, 0, s>>>(pcm, clips, tiles, basis, melw, melb0, logmel, clip_key, flag);
     return hipGetLastError();
 }
 

@@ -49,9 +49,12 @@ hipError_t init_flags(hipStream_t s, int* clip_key, int n_clips, int* flag);
 // 32 samples][cos, sin][hi, mid, lo][64 lanes] x 8 bf16 (lane l: bin
 // 16 chunk + l % 16, samples 32 kb + 8 (l / 16) .. + 7; zero past bin 200 and
 // sample 399).
+// melw / melb0: mel band m weighs power bins melb0[m] .. + kMelTaps - 1 with
+// melw[m][0 .. kMelTaps - 1] (zero past the filter's support).
 constexpr int kDftKBlocks = 13;
+constexpr int kMelTaps = 12;
 hipError_t frontend(hipStream_t s, const float* pcm, const ClipInfo* clips, const FrontTile* tiles,
-                    int n_tiles, const uint4* basis, const float* fbB, const int* fb_range,
+                    int n_tiles, const uint4* basis, const float* melw, const int* melb0,
                     float* logmel, int* clip_key, int* flag);
 hipError_t normalize(hipStream_t s, float* logmel, const ClipInfo* clips, const FrontTile* tiles,
                      int n_tiles, const int* clip_key);
