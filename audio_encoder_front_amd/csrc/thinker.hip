@@ -170,10 +170,14 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
     __shared__ __align__(16) char vts[kTHd * VR];
 
     // workgroup = (prompt, HPW consecutive query heads of one KV head, 64 queries);
-    // waves 4 i .. 4 i + 3 take query head i of the group, 16 queries each
-    const int qg = blockIdx.x % qgroups;
-    const int ph = blockIdx.x / qgroups;
+    // waves 4 i .. 4 i + 3 take query head i of the group, 16 queries each.
+    // Causal work grows with the query group, so the groups are dispatched
+    // longest first (all (prompt, head group) pairs of the last query group,
+    // then the one before, ...): the short ones fill the tail.
     const int hgroups = hq / HPW;
+    const int nph = (int)(gridDim.x / qgroups);              // (prompt, head group) pairs
+    const int qg = qgroups - 1 - (int)(blockIdx.x / nph);
+    const int ph = (int)(blockIdx.x % nph);
     const int seg = ph / hgroups;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = (ph % hgroups) * HPW + (wave >> 2);
@@ -200,9 +204,11 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
     for (int dt = 0; dt < kTHd / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int kend = min(n, qg * 64 + 64);                   // causal: no key beyond the group's last query
-    for (int k0 = 0; k0 < kend; k0 += kTKB) {
-        __syncthreads();                                     // previous block consumed
-        uint4 kv[NCH], vv[NCH];
+    // K / V rows of a key block go global -> registers one block ahead (the
+    // loads of block k0 + kTKB are in flight while block k0 is multiplied),
+    // then registers -> LDS (V transposed) at the top of the next iteration.
+    uint4 kv[NCH], vv[NCH];
+    auto load_block = [&](int k0) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int idx = tid + c * NT;
@@ -214,6 +220,10 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
                 vv[c] = ld16(vbase_p + off);
             }
         }
+    };
+    load_block(0);
+    for (int k0 = 0; k0 < kend; k0 += kTKB) {
+        __syncthreads();                                     // previous block consumed
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int idx = tid + c * NT;
@@ -224,6 +234,7 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
             for (int e = 0; e < PER; ++e) *reinterpret_cast<T*>(vts + (ch * PER + e) * VR + t * sizeof(T)) = ve[e];
         }
         __syncthreads();
+        if (k0 + kTKB < kend) load_block(k0 + kTKB);
         if (!active || k0 > qt * 16 + 15) continue;          // this wave's queries precede the block
         f32x4 sacc[kTKB / 16];
 #pragma unroll
