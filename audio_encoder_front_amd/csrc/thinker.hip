@@ -207,12 +207,19 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
     // K / V rows of a key block go global -> registers one block ahead (the
     // loads of block k0 + kTKB are in flight while block k0 is multiplied),
     // then registers -> LDS (V transposed) at the top of the next iteration.
+    // Chunk c of this thread is key row key_of(c), 16-byte column tid % CPR.
+    // bf16: the thread's keys come in adjacent pairs (2 p, 2 p + 1), so the
+    // transposed V store writes both keys of a dimension as one 4-byte word.
+    static_assert(sizeof(T) != 2 || NCH % 2 == 0, "key pairs");
+    auto key_of = [&](int c) {
+        if constexpr (sizeof(T) == 2) return 2 * (tid / CPR + (c / 2) * (NT / CPR)) + (c & 1);
+        else return (tid + c * NT) / CPR;
+    };
     uint4 kv[NCH], vv[NCH];
     auto load_block = [&](int k0) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int idx = tid + c * NT;
-            const int t = idx / CPR, ch = idx % CPR;
+            const int t = key_of(c), ch = tid % CPR;
             kv[c] = vv[c] = zero16();
             if (k0 + t < n) {
                 const size_t off = (size_t)(s0 + k0 + t) * ld + ch * PER;
@@ -224,14 +231,33 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
     load_block(0);
     for (int k0 = 0; k0 < kend; k0 += kTKB) {
         __syncthreads();                                     // previous block consumed
+        {
+            const int ch = tid % CPR;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int idx = tid + c * NT;
-            const int t = idx / CPR, ch = idx % CPR;
-            st16(ks + t * KR + ch * 16, kv[c]);
-            const T* ve = reinterpret_cast<const T*>(&vv[c]);
+            for (int c = 0; c < NCH; ++c) st16(ks + key_of(c) * KR + ch * 16, kv[c]);
+            if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int e = 0; e < PER; ++e) *reinterpret_cast<T*>(vts + (ch * PER + e) * VR + t * sizeof(T)) = ve[e];
+                for (int c = 0; c < NCH; c += 2) {
+                    const int t = key_of(c);              // even; t + 1 is chunk c + 1's key
+                    const unsigned* va = reinterpret_cast<const unsigned*>(&vv[c]);
+                    const unsigned* vb = reinterpret_cast<const unsigned*>(&vv[c + 1]);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {         // dims 2 w, 2 w + 1 of the chunk
+                        const unsigned lo = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);   // (a.d0, b.d0)
+                        const unsigned hi = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);   // (a.d1, b.d1)
+                        *reinterpret_cast<unsigned*>(vts + (ch * PER + 2 * w) * VR + t * 2) = lo;
+                        *reinterpret_cast<unsigned*>(vts + (ch * PER + 2 * w + 1) * VR + t * 2) = hi;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const T* ve = reinterpret_cast<const T*>(&vv[c]);
+#pragma unroll
+                    for (int e = 0; e < PER; ++e)
+                        *reinterpret_cast<T*>(vts + (ch * PER + e) * VR + key_of(c) * sizeof(T)) = ve[e];
+                }
+            }
         }
         __syncthreads();
         if (k0 + kTKB < kend) load_block(k0 + kTKB);
