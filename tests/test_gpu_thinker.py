@@ -118,3 +118,18 @@ def test_bf16_thinker_shapes(dims, seed, spec):
     print("case: bf16 thinker", dims.hidden, [len(p[0]) for p in prompts], flush=True)
     hid, lg = _run(dims, W, prompts, audio)
     print("bf16 thinker worst (hidden, logits)", _check(dims, W, prompts, audio, hid, lg), flush=True)
+
+
+def test_tiny_thinker_ragged_widths():
+    """Widths that leave partial 16-byte chunks in the GEMM epilogues: a vocab
+    of 1003 (the fp32 logits rows end 3 values into a chunk) and an FFN of 48
+    (SwiGLU output of 48 features from a 96-row gate/up GEMM), one layer."""
+    d = ST.ThinkerDims(hidden=128, n_layers=1, n_q_heads=2, n_kv_heads=1, ffn_dim=48, vocab=1003, dtype="f32")
+    W = ST.make_weights(d, 230)
+    prompts = _prompts([9, 1], d.vocab, 231)
+    n_audio = sum(p[2] for p in prompts)
+    audio = ST.make_audio_states(n_audio, d.hidden, [232, 0])
+    print("case: tiny thinker, vocab 1003, ffn 48", flush=True)
+    hid, lg = _run(d, W, prompts, audio)
+    assert lg.shape == (len(prompts), d.vocab)
+    print("ragged-width thinker worst (hidden, logits)", _check(d, W, prompts, audio, hid, lg), flush=True)
