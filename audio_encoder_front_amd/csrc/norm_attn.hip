@@ -177,11 +177,19 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     // K and V rows of this head (16 bytes per load, every load issued before
     // any LDS store); rows at or beyond n are zeros.  V is stored transposed.
     constexpr int NCH = (ROWS * CPR + 255) / 256;  // 16-byte chunks per thread per matrix
+    // Chunk q of this thread is key row key_of(q), 16-byte column tid % CPR;
+    // bf16 keys come in adjacent pairs (2 p, 2 p + 1) so that the transposed
+    // V store writes both keys of a dimension as one 4-byte word.
+    static_assert(sizeof(T) != 2 || NCH % 2 == 0, "key pairs");
+    auto key_of = [&](int q) {
+        if constexpr (sizeof(T) == 2) return 2 * (tid / CPR + (q / 2) * (256 / CPR)) + (q & 1);
+        else return (tid + q * 256) / CPR;
+    };
+    const int c = tid % CPR;
     uint4 kv[NCH], vv[NCH];
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-        const int idx = tid + q * 256;
-        const int t = idx / CPR, c = idx % CPR;
+        const int t = key_of(q);
         kv[q] = vv[q] = zero16();
         if (t < n) {
             const T* row = qkv + (size_t)(s0 + t) * ld + d + h * kHd + c * PER;
@@ -191,14 +199,34 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     }
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-        const int idx = tid + q * 256;
-        const int t = idx / CPR, c = idx % CPR;
-        if (ROWS * CPR % 256 != 0 && t >= ROWS) continue;
-        st16(ks + t * QR + c * 16, kv[q]);
-        const T* ve = reinterpret_cast<const T*>(&vv[q]);
+        const int t = key_of(q);
+        if (t < ROWS) st16(ks + t * QR + c * 16, kv[q]);
+    }
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            *reinterpret_cast<T*>(vts + (c * PER + e) * VR + t * sizeof(T)) = ve[e];
+        for (int q = 0; q < NCH; q += 2) {
+            const int t = key_of(q);                   // even; t + 1 is chunk q + 1's key
+            if (t >= ROWS) continue;                   // ROWS is even: the pair is in or out together
+            const unsigned* va = reinterpret_cast<const unsigned*>(&vv[q]);
+            const unsigned* vb = reinterpret_cast<const unsigned*>(&vv[q + 1]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {              // dimensions 2 w, 2 w + 1 of the chunk
+                *reinterpret_cast<unsigned*>(vts + (c * PER + 2 * w) * VR + t * 2) =
+                    __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);   // (key t, key t + 1) of dim 2 w
+                *reinterpret_cast<unsigned*>(vts + (c * PER + 2 * w + 1) * VR + t * 2) =
+                    __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);   // ... of dim 2 w + 1
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            const int t = key_of(q);
+            if (t >= ROWS) continue;
+            const T* ve = reinterpret_cast<const T*>(&vv[q]);
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                *reinterpret_cast<T*>(vts + (c * PER + e) * VR + t * sizeof(T)) = ve[e];
+        }
     }
     __syncthreads();
 
