@@ -27,12 +27,15 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <typename T>
+template <typename T, int NQ>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, int M, int d,
                                                         const float* __restrict__ g,
                                                         const float* __restrict__ b, T* __restrict__ out) {
-    // Each wave walks rows row0, row0 + stride, ...; the next row's loads are
-    // issued before the current row is reduced, keeping two rows in flight.
+    // One wave per row (a row of d <= 256 NQ values is NQ float4 per lane).
+    // The grid normally covers every row at once; past that, each wave walks
+    // rows row0, row0 + stride, ... with the next row's loads issued before
+    // the current row is reduced.  gamma / beta are loaded with the row, so
+    // their (L2) latency hides under the row's.
     const int lane = threadIdx.x & 63;
     const int stride = gridDim.x * 4;
     const int d4 = d >> 2;
@@ -41,46 +44,50 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
     auto load_row = [&](int row, float4* v) {
         const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * d);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int i = lane + 64 * q;
             if (i < d4) v[q] = xr[i];
         }
     };
     int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M) return;
-    float4 cur[8], nxt[8];
+    float4 cur[NQ], nxt[NQ], gg[NQ], bb[NQ];
     load_row(row, cur);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int i = lane + 64 * q;
+        if (i < d4) { gg[q] = g4[i]; bb[q] = b4[i]; }
+    }
     for (; row < M; row += stride) {
         if (row + stride < M) load_row(row + stride, nxt);
         float s = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int i = lane + 64 * q;
             if (i < d4) s += (cur[q].x + cur[q].y) + (cur[q].z + cur[q].w);
         }
         const float mean = wave_sum(s) / (float)d;
         float ss = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int i = lane + 64 * q;
             if (i < d4) {
-                const float a = cur[q].x - mean, bb = cur[q].y - mean, c = cur[q].z - mean, e = cur[q].w - mean;
-                ss += (a * a + bb * bb) + (c * c + e * e);
+                const float a = cur[q].x - mean, e1 = cur[q].y - mean, c = cur[q].z - mean, e = cur[q].w - mean;
+                ss += (a * a + e1 * e1) + (c * c + e * e);
             }
         }
         const float rstd = rsqrtf(wave_sum(ss) / (float)d + kLnEps);
         T* o = out + (size_t)row * d;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int i = lane + 64 * q;
-            if (i < d4) {
-                const float4 gg = g4[i], bb = b4[i];
-                store4(o + 4 * i, (cur[q].x - mean) * rstd * gg.x + bb.x, (cur[q].y - mean) * rstd * gg.y + bb.y,
-                       (cur[q].z - mean) * rstd * gg.z + bb.z, (cur[q].w - mean) * rstd * gg.w + bb.w);
-            }
+            if (i < d4)
+                store4(o + 4 * i, (cur[q].x - mean) * rstd * gg[q].x + bb[q].x,
+                       (cur[q].y - mean) * rstd * gg[q].y + bb[q].y, (cur[q].z - mean) * rstd * gg[q].z + bb[q].z,
+                       (cur[q].w - mean) * rstd * gg[q].w + bb[q].w);
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
+        for (int q = 0; q < NQ; ++q) cur[q] = nxt[q];
     }
 }
 
@@ -88,8 +95,10 @@ template <typename T>
 hipError_t layernorm(hipStream_t s, const float* x, int M, int d, const float* g, const float* b, T* out) {
     if (M <= 0) return hipSuccess;
     if (d % 4 || d > 2048) return hipErrorInvalidValue;
-    const int blocks = std::min((M + 3) / 4, 256 * 4);   // four waves per SIMD, each walking rows
-    layernorm_kernel<T><<<blocks, 256, 0, s>>>(x, M, d, g, b, out);
+    // One wave per row up to 64K rows (every row's loads in flight at once).
+    const int blocks = std::min((M + 3) / 4, 16384);
+    if (d <= 1024) layernorm_kernel<T, 4><<<blocks, 256, 0, s>>>(x, M, d, g, b, out);
+    else layernorm_kernel<T, 8><<<blocks, 256, 0, s>>>(x, M, d, g, b, out);
     return hipGetLastError();
 }
 
