@@ -114,10 +114,11 @@ hipError_t layernorm(hipStream_t s, const float* x, int M, int d, const float* g
 constexpr int kHd = 64;
 
 // LDS rows: K rows of the head (64 values + 16 bytes of padding) and V^T
-// rows (one per head dimension, ROWS keys + padding), for ROWS keys.
+// rows (head dimension d at row vt_row(d), ROWS keys + padding), for ROWS
+// keys.
 template <typename T, int ROWS> struct AttnLds {
     static constexpr int qrow = 64 * (int)sizeof(T) + 16;
-    static constexpr int vrow = (int)sizeof(T) * ROWS + (sizeof(T) == 2 ? 8 : 16);
+    static constexpr int vrow = (int)sizeof(T) * ROWS + (sizeof(T) == 2 ? 40 : 16);
 };
 
 // P.V over one 32-key step (bf16) or one 16-key tile (fp32), accumulate o[dt].
@@ -132,7 +133,7 @@ __device__ __forceinline__ void pv_step(bf16, const char* vt, int kbase, int fr,
     for (int r = 0; r < 4; ++r) { pb[r] = (bf16)p[t0][r]; pb[4 + r] = (bf16)p[t0 + 1][r]; }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const char* row = vt + (dt * 16 + fr) * VR;
+        const char* row = vt + vt_row(dt * 16 + fr) * VR;
         const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 4 * fg));
         const uint2 hi = HALF ? make_uint2(0u, 0u) : *reinterpret_cast<const uint2*>(row + 2 * (kbase + 16 + 4 * fg));
         const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -144,7 +145,7 @@ __device__ __forceinline__ void pv_step(float, const char* vt, int kbase, int fr
                                         int t0, f32x4* o) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const char* row = vt + (dt * 16 + fr) * VR;
+        const char* row = vt + vt_row(dt * 16 + fr) * VR;
         const float4 va = *reinterpret_cast<const float4*>(row + 4 * (kbase + 4 * fg));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, p[t0][0], o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, p[t0][1], o[dt], 0, 0, 0);
@@ -220,9 +221,9 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
             const unsigned* vb = reinterpret_cast<const unsigned*>(&vv[q + 1]);
 #pragma unroll
             for (int w = 0; w < 4; ++w) {              // dimensions 2 w, 2 w + 1 of the chunk
-                *reinterpret_cast<unsigned*>(vts + (c * PER + 2 * w) * VR + t * 2) =
+                *reinterpret_cast<unsigned*>(vts + vt_row(c * PER + 2 * w) * VR + t * 2) =
                     __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);   // (key t, key t + 1) of dim 2 w
-                *reinterpret_cast<unsigned*>(vts + (c * PER + 2 * w + 1) * VR + t * 2) =
+                *reinterpret_cast<unsigned*>(vts + vt_row(c * PER + 2 * w + 1) * VR + t * 2) =
                     __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);   // ... of dim 2 w + 1
             }
         }
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
             const T* ve = reinterpret_cast<const T*>(&vv[q]);
 #pragma unroll
             for (int e = 0; e < PER; ++e)
-                *reinterpret_cast<T*>(vts + (c * PER + e) * VR + t * sizeof(T)) = ve[e];
+                *reinterpret_cast<T*>(vts + vt_row(c * PER + e) * VR + t * sizeof(T)) = ve[e];
         }
     }
     __syncthreads();
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(256) void attention_long_kernel(const T* __restrict
             const T* ve = reinterpret_cast<const T*>(&vv[q]);
 #pragma unroll
             for (int e = 0; e < PER; ++e)
-                *reinterpret_cast<T*>(vts + (c * PER + e) * VR + t * sizeof(T)) = ve[e];
+                *reinterpret_cast<T*>(vts + vt_row(c * PER + e) * VR + t * sizeof(T)) = ve[e];
         }
         __syncthreads();
         if (!active) continue;

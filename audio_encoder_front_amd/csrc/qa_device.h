@@ -26,6 +26,14 @@ __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4
 //         k index 4g+s of the block, identically for A and B, so the product
 //         is the same sum in a permuted order.
 // The result lane l holds D[4g + r][l % 16], r = 0..3.
+// Row of head dimension d in the transposed-V LDS tiles of the attention
+// kernels: dims are XOR-permuted within each group of 8 by the group index.
+// One store instruction writes dims 8 c + e of many 16-byte chunks c at once,
+// rows a multiple of 8 apart that an unpermuted layout maps to few LDS banks;
+// the permutation spreads them.  The fragment reads (16 consecutive dims)
+// are unaffected.  The row paddings that go with it were chosen by timing.
+__device__ __forceinline__ int vt_row(int d) { return d ^ ((d >> 3) & 7); }
+
 __device__ __forceinline__ void mfma_kblock(bf16, const uint4& a, const uint4& b, f32x4& acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);

@@ -121,56 +121,79 @@ constexpr int kTKB = 64;                     // keys per block
 template <typename T> struct TAttnLds;
 template <> struct TAttnLds<bf16> {
     static constexpr int krow = kTHd * 2 + 16;      // bytes per K row (padded)
-    static constexpr int vrow = kTKB * 2 + 8;       // bytes per V^T row (d index)
+    static constexpr int vrow = kTKB * 2 + 24;      // bytes per V^T row (row vt_row(d) for dim d)
 };
 template <> struct TAttnLds<float> {
     static constexpr int krow = kTHd * 4 + 16;
     static constexpr int vrow = kTKB * 4 + 16;
 };
 
-__device__ __forceinline__ void tpv_step(bf16, const char* vt, int kbase, int fr, int fg, const f32x4* p, int t0,
-                                         f32x4* o) {
+// P.V for the QT query tiles of a wave over one 32-key step (bf16) or one
+// 16-key tile (fp32): each V^T fragment is read from LDS once and multiplied
+// into every query tile.  bf16: o[u][kTHd / 16] (the extra tile) accumulates
+// the probability sums; its A operand is all ones, so each of its rows is
+// sum_k p[k][query], taken over the same bf16-rounded probabilities that
+// weight V.
+template <int QT>
+__device__ __forceinline__ void tpv_step(bf16, const char* vt, int kbase, int fr, int fg,
+                                         const f32x4 (*p)[kTKB / 16], int t0, f32x4 (*o)[kTHd / 16 + 1]) {
     // slots 0..3: keys kbase + 4g + r (tile t0), 4..7: kbase + 16 + 4g + r (tile t0 + 1)
-    bf16x8 pb;
+    bf16x8 pb[QT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { pb[r] = (bf16)p[t0][r]; pb[4 + r] = (bf16)p[t0 + 1][r]; }
+    for (int u = 0; u < QT; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { pb[u][r] = (bf16)p[u][t0][r]; pb[u][4 + r] = (bf16)p[u][t0 + 1][r]; }
+    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);   // bf16 1.0 x 8
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+        o[u][kTHd / 16] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), pb[u], o[u][kTHd / 16], 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < kTHd / 16; ++dt) {
-        const char* row = vt + (dt * 16 + fr) * TAttnLds<bf16>::vrow;
+        const char* row = vt + vt_row(dt * 16 + fr) * TAttnLds<bf16>::vrow;
         const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 4 * fg));
         const uint2 hi = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 16 + 4 * fg));
-        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[dt], 0, 0, 0);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int u = 0; u < QT; ++u) o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[u], o[u][dt], 0, 0, 0);
     }
 }
-__device__ __forceinline__ void tpv_step(float, const char* vt, int kbase, int fr, int fg, const f32x4* p, int t0,
-                                         f32x4* o) {
+template <int QT>
+__device__ __forceinline__ void tpv_step(float, const char* vt, int kbase, int fr, int fg,
+                                         const f32x4 (*p)[kTKB / 16], int t0, f32x4 (*o)[kTHd / 16 + 1]) {
 #pragma unroll
     for (int dt = 0; dt < kTHd / 16; ++dt) {
-        const char* row = vt + (dt * 16 + fr) * TAttnLds<float>::vrow;
+        const char* row = vt + vt_row(dt * 16 + fr) * TAttnLds<float>::vrow;
         const float4 va = *reinterpret_cast<const float4*>(row + 4 * (kbase + 4 * fg));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, p[t0][0], o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, p[t0][1], o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, p[t0][2], o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, p[t0][3], o[dt], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+            o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, p[u][t0][0], o[u][dt], 0, 0, 0);
+            o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, p[u][t0][1], o[u][dt], 0, 0, 0);
+            o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, p[u][t0][2], o[u][dt], 0, 0, 0);
+            o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, p[u][t0][3], o[u][dt], 0, 0, 0);
+        }
     }
 }
 
-template <typename T, int HPW>
-__global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* __restrict__ qkv,
-                                                                      const int* __restrict__ cu, int hq, int hkv,
-                                                                      int qgroups, T* __restrict__ out) {
+// Workgroup = (prompt, HPW consecutive query heads of one KV head, 64
+// queries); each head has 4 / QT waves, each taking QT consecutive 16-query
+// tiles, so every K and V fragment read from LDS feeds QT MFMAs.
+template <typename T, int HPW, int QT>
+__global__ __launch_bounds__(64 * HPW * (4 / QT)) __attribute__((amdgpu_waves_per_eu(2))) void thinker_attention_kernel(const T* __restrict__ qkv,
+                                                                                const int* __restrict__ cu, int hq,
+                                                                                int hkv, int qgroups,
+                                                                                T* __restrict__ out) {
     constexpr int KR = TAttnLds<T>::krow, VR = TAttnLds<T>::vrow;
     constexpr int PER = Elem<T>::per16;
     constexpr int CPR = kTHd / PER;                          // 16-byte chunks per head row
     constexpr int KBN = kTHd * (int)sizeof(T) / 64;          // 64-byte MFMA K blocks per head row
-    constexpr int NT = 256 * HPW;                            // threads
+    constexpr int WPH = 4 / QT;                              // waves per head
+    constexpr int NT = 64 * HPW * WPH;                       // threads
     constexpr int NCH = kTKB * CPR / NT;                     // chunks per thread per key block
+    static_assert(4 % QT == 0 && kTKB * CPR % NT == 0, "tiling");
     __shared__ __align__(16) char ks[kTKB * KR];
     __shared__ __align__(16) char vts[kTHd * VR];
 
-    // workgroup = (prompt, HPW consecutive query heads of one KV head, 64 queries);
-    // waves 4 i .. 4 i + 3 take query head i of the group, 16 queries each.
     // Causal work grows with the query group, so the groups are dispatched
     // longest first (all (prompt, head group) pairs of the last query group,
     // then the one before, ...): the short ones fill the tail.
@@ -180,7 +203,7 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
     const int ph = (int)(blockIdx.x % nph);
     const int seg = ph / hgroups;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = (ph % hgroups) * HPW + (wave >> 2);
+    const int h = (ph % hgroups) * HPW + wave / WPH;
     const int kvh = h / (hq / hkv);                          // the same for all HPW heads
     const int s0 = cu[seg], n = cu[seg + 1] - s0;
     if (qg * 64 >= n) return;                                // whole workgroup idle (uniform)
@@ -188,25 +211,39 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
     const size_t ld = (size_t)(hq + 2 * hkv) * kTHd;
     const T* kbase_p = qkv + (size_t)hq * kTHd + (size_t)kvh * kTHd;
     const T* vbase_p = kbase_p + (size_t)hkv * kTHd;
-    const int qt = qg * 4 + (wave & 3);
-    const bool active = qt * 16 < n;                         // wave-uniform
-    const int q = qt * 16 + fr;                              // this lane's query (within the prompt)
-    uint4 qf[KBN];
-    {
+    const int qt0 = qg * 4 + (wave % WPH) * QT;              // this wave's first query tile
+    const bool active = qt0 * 16 < n;                        // wave-uniform
+    uint4 qf[QT][KBN];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+        const int q = (qt0 + u) * 16 + fr;
         const T* row = qkv + (size_t)(s0 + q) * ld + h * kTHd + fg * PER;
 #pragma unroll
-        for (int kb = 0; kb < KBN; ++kb) qf[kb] = q < n ? ld16(row + kb * (64 / (int)sizeof(T))) : zero16();
+        for (int kb = 0; kb < KBN; ++kb) qf[u][kb] = q < n ? ld16(row + kb * (64 / (int)sizeof(T))) : zero16();
     }
     const float sc = 0.08838834764831845f * 1.4426950408889634f;   // 1/sqrt(128) * log2(e)
-    float m = -INFINITY, l = 0.f;
-    f32x4 o[kTHd / 16];
+    // Online softmax in log2 units.  m is the reference the probabilities are
+    // taken against, 2^(s sc - m); it moves to the running maximum only when
+    // some lane's block maximum exceeds it by more than kLazy (the decision is
+    // wave-uniform), so most blocks skip the rescaling of o and keep p below
+    // 2^kLazy.  -inf while the lane's query has seen no key.
+    constexpr float kLazy = 8.f;
+    constexpr bool kSumMfma = sizeof(T) == 2;                // row sums in o[u][kTHd / 16] (bf16)
+    float m[QT], l[QT];
+    f32x4 o[QT][kTHd / 16 + 1];
 #pragma unroll
-    for (int dt = 0; dt < kTHd / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < QT; ++u) {
+        m[u] = -INFINITY;
+        l[u] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt <= kTHd / 16; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int kend = min(n, qg * 64 + 64);                   // causal: no key beyond the group's last query
-    // K / V rows of a key block go global -> registers one block ahead (the
-    // loads of block k0 + kTKB are in flight while block k0 is multiplied),
-    // then registers -> LDS (V transposed) at the top of the next iteration.
+    // K / V rows of a key block go global -> registers two blocks ahead (the
+    // loads of blocks k0 + kTKB and k0 + 2 kTKB are in flight while block k0
+    // is multiplied; two register sets alternate), then registers -> LDS (V
+    // transposed) at the top of the block's own iteration.
     // Chunk c of this thread is key row key_of(c), 16-byte column tid % CPR.
     // bf16: the thread's keys come in adjacent pairs (2 p, 2 p + 1), so the
     // transposed V store writes both keys of a dimension as one 4-byte word.
@@ -215,8 +252,9 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
         if constexpr (sizeof(T) == 2) return 2 * (tid / CPR + (c / 2) * (NT / CPR)) + (c & 1);
         else return (tid + c * NT) / CPR;
     };
-    uint4 kv[NCH], vv[NCH];
-    auto load_block = [&](int k0) {
+    using Regs = uint4[NCH];
+    Regs kvA, vvA, kvB, vvB;
+    auto load_block = [&](int k0, Regs& kv, Regs& vv) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int t = key_of(c), ch = tid % CPR;
@@ -228,8 +266,7 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
             }
         }
     };
-    load_block(0);
-    for (int k0 = 0; k0 < kend; k0 += kTKB) {
+    auto process = [&](int k0, Regs& kv, Regs& vv) {
         __syncthreads();                                     // previous block consumed
         {
             const int ch = tid % CPR;
@@ -245,8 +282,8 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
                     for (int w = 0; w < 4; ++w) {         // dims 2 w, 2 w + 1 of the chunk
                         const unsigned lo = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);   // (a.d0, b.d0)
                         const unsigned hi = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);   // (a.d1, b.d1)
-                        *reinterpret_cast<unsigned*>(vts + (ch * PER + 2 * w) * VR + t * 2) = lo;
-                        *reinterpret_cast<unsigned*>(vts + (ch * PER + 2 * w + 1) * VR + t * 2) = hi;
+                        *reinterpret_cast<unsigned*>(vts + vt_row(ch * PER + 2 * w) * VR + t * 2) = lo;
+                        *reinterpret_cast<unsigned*>(vts + vt_row(ch * PER + 2 * w + 1) * VR + t * 2) = hi;
                     }
                 }
             } else {
@@ -255,87 +292,110 @@ __global__ __launch_bounds__(256 * HPW) void thinker_attention_kernel(const T* _
                     const T* ve = reinterpret_cast<const T*>(&vv[c]);
 #pragma unroll
                     for (int e = 0; e < PER; ++e)
-                        *reinterpret_cast<T*>(vts + (ch * PER + e) * VR + key_of(c) * sizeof(T)) = ve[e];
+                        *reinterpret_cast<T*>(vts + vt_row(ch * PER + e) * VR + key_of(c) * sizeof(T)) = ve[e];
                 }
             }
         }
         __syncthreads();
-        if (k0 + kTKB < kend) load_block(k0 + kTKB);
-        if (!active || k0 > qt * 16 + 15) continue;          // this wave's queries precede the block
-        f32x4 sacc[kTKB / 16];
+        if (k0 + 2 * kTKB < kend) load_block(k0 + 2 * kTKB, kv, vv);
+        if (!active || k0 > (qt0 + QT) * 16 - 1) return;     // every query of the wave precedes the block
+        f32x4 sacc[QT][kTKB / 16];
 #pragma unroll
-        for (int kt = 0; kt < kTKB / 16; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < QT; ++u)
+#pragma unroll
+            for (int kt = 0; kt < kTKB / 16; ++kt) sacc[u][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
 #pragma unroll
             for (int kt = 0; kt < kTKB / 16; ++kt) {
                 const uint4 kf = ld16(ks + (kt * 16 + fr) * KR + fg * 16 + kb * 64);
-                mfma_kblock(T(), kf, qf[kb], sacc[kt]);
+#pragma unroll
+                for (int u = 0; u < QT; ++u) mfma_kblock(T(), kf, qf[u][kb], sacc[u][kt]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // lane holds S^T[key k0 + 16 kt + 4 fg + r][query fr]
-        float bm = -INFINITY;
-        if (k0 + kTKB - 1 <= qt * 16 && k0 + kTKB <= n) {   // whole block visible to every query of the wave
+        // lane holds S^T[key k0 + 16 kt + 4 fg + r][query (qt0 + u) 16 + fr] (unscaled)
+        const bool full = k0 + kTKB - 1 <= qt0 * 16 && k0 + kTKB <= n;   // visible to every query of the wave
 #pragma unroll
-            for (int kt = 0; kt < kTKB / 16; ++kt)
+        for (int u = 0; u < QT; ++u) {
+            const int q = (qt0 + u) * 16 + fr;
+            float bm = -INFINITY;
+            if (full) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sacc[kt][r] *= sc;
-                    bm = fmaxf(bm, sacc[kt][r]);
-                }
-        } else {
+                for (int kt = 0; kt < kTKB / 16; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < kTKB / 16; ++kt)
+                    for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sacc[u][kt][r]);
+            } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = k0 + kt * 16 + 4 * fg + r;
-                    const float v = (key <= q && key < n) ? sacc[kt][r] * sc : -INFINITY;
-                    sacc[kt][r] = v;
-                    bm = fmaxf(bm, v);
-                }
-        }
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bm);
-        // a query past the prompt end (q >= n) sees no key: keep it finite
-        const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m - mref);
-        float bs = 0.f;
+                for (int kt = 0; kt < kTKB / 16; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < kTKB / 16; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = __builtin_amdgcn_exp2f(sacc[kt][r] - mref);
-                sacc[kt][r] = p;
-                bs += p;
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = k0 + kt * 16 + 4 * fg + r;
+                        const float v = (key <= q && key < n) ? sacc[u][kt][r] : -INFINITY;
+                        sacc[u][kt][r] = v;
+                        bm = fmaxf(bm, v);
+                    }
             }
-        bs += __shfl_xor(bs, 16);
-        bs += __shfl_xor(bs, 32);
-        l = l * alpha + bs;
-        m = mn;
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float bms = bm * sc;                       // block maximum in log2 units (sc > 0)
+            if (__builtin_amdgcn_ballot_w64(bms > m[u] + kLazy) != 0) {
+                const float mn = fmaxf(m[u], bms);
+                // alpha = 0 while nothing has been accumulated (m = -inf)
+                const float alpha = m[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[u] - mn);
 #pragma unroll
-        for (int dt = 0; dt < kTHd / 16; ++dt) o[dt] = o[dt] * alpha;
+                for (int dt = 0; dt <= kTHd / 16; ++dt) o[u][dt] = o[u][dt] * alpha;
+                l[u] *= alpha;
+                m[u] = mn;
+            }
+            // a query that has seen no key keeps m = -inf: take 0 as the reference
+            const float mref = m[u] == -INFINITY ? 0.f : m[u];
+            float bs = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < kTKB / 16; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][kt][r], sc, -mref));
+                    sacc[u][kt][r] = p;
+                    if constexpr (!kSumMfma) bs += p;
+                }
+            if constexpr (!kSumMfma) {
+                bs += __shfl_xor(bs, 16);
+                bs += __shfl_xor(bs, 32);
+                l[u] += bs;
+            }
+        }
         if (sizeof(T) == 2) {
 #pragma unroll
             for (int st = 0; st < kTKB / 32; ++st) {
-                tpv_step(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+                tpv_step<QT>(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
             for (int kt = 0; kt < kTKB / 16; ++kt) {
-                tpv_step(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
+                tpv_step<QT>(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        };
+    load_block(0, kvA, vvA);
+    if (kTKB < kend) load_block(kTKB, kvB, vvB);
+    for (int k0 = 0; k0 < kend; k0 += 2 * kTKB) {
+        process(k0, kvA, vvA);
+        if (k0 + kTKB < kend) process(k0 + kTKB, kvB, vvB);
     }
-    if (active && q < n) {
-        const float inv = 1.0f / l;
-        T* orow = out + (size_t)(s0 + q) * hq * kTHd + h * kTHd;
 #pragma unroll
-        for (int dt = 0; dt < kTHd / 16; ++dt)
-            store4(orow + dt * 16 + 4 * fg, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    for (int u = 0; u < QT; ++u) {
+        const int q = (qt0 + u) * 16 + fr;
+        if (active && q < n) {
+            const float inv = 1.0f / (kSumMfma ? o[u][kTHd / 16][0] : l[u]);
+            T* orow = out + (size_t)(s0 + q) * hq * kTHd + h * kTHd;
+#pragma unroll
+            for (int dt = 0; dt < kTHd / 16; ++dt)
+                store4(orow + dt * 16 + 4 * fg, o[u][dt][0] * inv, o[u][dt][1] * inv, o[u][dt][2] * inv,
+                       o[u][dt][3] * inv);
+        }
     }
 }
 
@@ -377,10 +437,12 @@ hipError_t thinker_attention(hipStream_t s, const T* qkv, const int* cu, int n_p
     const int hpw = (hq / hkv) % 2 == 0 ? 2 : 1;
     const int64_t blocks = (int64_t)n_prompts * (hq / hpw) * qgroups;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    // bf16: two 16-query tiles per wave; fp32 (register-heavy): one
+    constexpr int QT = sizeof(T) == 2 ? 2 : 1;
     if (hpw == 2)
-        thinker_attention_kernel<T, 2><<<(unsigned)blocks, 512, 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
+        thinker_attention_kernel<T, 2, QT><<<(unsigned)blocks, 128 * (4 / QT), 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
     else
-        thinker_attention_kernel<T, 1><<<(unsigned)blocks, 256, 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
+        thinker_attention_kernel<T, 1, QT><<<(unsigned)blocks, 64 * (4 / QT), 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
     return hipGetLastError();
 }
 
