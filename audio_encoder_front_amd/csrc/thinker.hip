@@ -108,15 +108,17 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* __restrict__ qkv, i
 // ---------------------------------------------------------------- attention
 // Causal grouped-query attention, head_dim 128, over packed prompts
 // [cu[i], cu[i + 1]); query head h reads KV head h / (hq / hkv).  One
-// workgroup per (prompt, query head, 64 queries), one 16-query tile per wave.
-// Per key block of 64: S^T = K Q^T on MFMA (a lane holds one query column),
-// the causal mask, an online softmax (running max / sum, the partial output
-// rescaled when the max grows) and O^T = V^T P^T with V^T transposed in LDS;
-// the workgroup stops at the block holding its last query.  When a KV head
-// serves an even number of query heads, a workgroup takes two of them (8
-// waves) so each K/V block is staged once for both.
+// workgroup per (prompt, query heads, query block): 128 queries in bf16 (two
+// 16-query tiles per wave), 64 in fp32 (one tile per wave).  Per key block of
+// 64: S^T = K Q^T on MFMA (a lane holds one query column), the causal mask,
+// an online softmax (running max / sum, the partial output rescaled when the
+// max grows past a margin) and O^T = V^T P^T with V^T transposed in LDS; the
+// workgroup stops at the block holding its last query.  When a KV head serves
+// an even number of query heads, a workgroup takes two of them so each K/V
+// block is staged once for both.
 constexpr int kTHd = 128;
 constexpr int kTKB = 64;                     // keys per block
+constexpr int kTQB = 128;                    // queries per workgroup (bf16)
 
 template <typename T> struct TAttnLds;
 template <> struct TAttnLds<bf16> {
@@ -175,11 +177,13 @@ __device__ __forceinline__ void tpv_step(float, const char* vt, int kbase, int f
     }
 }
 
-// Workgroup = (prompt, HPW consecutive query heads of one KV head, 64
-// queries); each head has 4 / QT waves, each taking QT consecutive 16-query
-// tiles, so every K and V fragment read from LDS feeds QT MFMAs.
-template <typename T, int HPW, int QT>
-__global__ __launch_bounds__(64 * HPW * (4 / QT)) __attribute__((amdgpu_waves_per_eu(2))) void thinker_attention_kernel(const T* __restrict__ qkv,
+// Workgroup = (prompt, HPW consecutive query heads of one KV head, QB
+// queries); each head has QB / 16 / QT waves, each taking QT consecutive
+// 16-query tiles, so every K and V fragment read from LDS feeds QT MFMAs.
+// Each workgroup streams every K/V block up to its diagonal, so the K/V
+// traffic (from L2 / the last-level cache) scales as 1 / QB.
+template <typename T, int HPW, int QT, int QB>
+__global__ __launch_bounds__(HPW * QB / QT * 4) __attribute__((amdgpu_waves_per_eu(2))) void thinker_attention_kernel(const T* __restrict__ qkv,
                                                                                 const int* __restrict__ cu, int hq,
                                                                                 int hkv, int qgroups,
                                                                                 T* __restrict__ out) {
@@ -187,10 +191,10 @@ __global__ __launch_bounds__(64 * HPW * (4 / QT)) __attribute__((amdgpu_waves_pe
     constexpr int PER = Elem<T>::per16;
     constexpr int CPR = kTHd / PER;                          // 16-byte chunks per head row
     constexpr int KBN = kTHd * (int)sizeof(T) / 64;          // 64-byte MFMA K blocks per head row
-    constexpr int WPH = 4 / QT;                              // waves per head
+    constexpr int WPH = QB / 16 / QT;                        // waves per head
     constexpr int NT = 64 * HPW * WPH;                       // threads
     constexpr int NCH = kTKB * CPR / NT;                     // chunks per thread per key block
-    static_assert(4 % QT == 0 && kTKB * CPR % NT == 0, "tiling");
+    static_assert(QB % (16 * QT) == 0 && kTKB * CPR % NT == 0, "tiling");
     __shared__ __align__(16) char ks[kTKB * KR];
     __shared__ __align__(16) char vts[kTHd * VR];
 
@@ -206,12 +210,12 @@ __global__ __launch_bounds__(64 * HPW * (4 / QT)) __attribute__((amdgpu_waves_pe
     const int h = (ph % hgroups) * HPW + wave / WPH;
     const int kvh = h / (hq / hkv);                          // the same for all HPW heads
     const int s0 = cu[seg], n = cu[seg + 1] - s0;
-    if (qg * 64 >= n) return;                                // whole workgroup idle (uniform)
+    if (qg * QB >= n) return;                                // whole workgroup idle (uniform)
     const int fr = lane & 15, fg = lane >> 4;
     const size_t ld = (size_t)(hq + 2 * hkv) * kTHd;
     const T* kbase_p = qkv + (size_t)hq * kTHd + (size_t)kvh * kTHd;
     const T* vbase_p = kbase_p + (size_t)hkv * kTHd;
-    const int qt0 = qg * 4 + (wave % WPH) * QT;              // this wave's first query tile
+    const int qt0 = qg * (QB / 16) + (wave % WPH) * QT;      // this wave's first query tile
     const bool active = qt0 * 16 < n;                        // wave-uniform
     uint4 qf[QT][KBN];
 #pragma unroll
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(64 * HPW * (4 / QT)) __attribute__((amdgpu_waves_pe
         for (int dt = 0; dt <= kTHd / 16; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int kend = min(n, qg * 64 + 64);                   // causal: no key beyond the group's last query
+    const int kend = min(n, qg * QB + QB);                   // causal: no key beyond the group's last query
     // K / V rows of a key block go global -> registers two blocks ahead (the
     // loads of blocks k0 + kTKB and k0 + 2 kTKB are in flight while block k0
     // is multiplied; two register sets alternate), then registers -> LDS (V
@@ -432,17 +436,19 @@ hipError_t thinker_attention(hipStream_t s, const T* qkv, const int* cu, int n_p
                              int max_len, T* out) {
     if (n_prompts <= 0) return hipSuccess;
     if (hkv <= 0 || hq % hkv) return hipErrorInvalidValue;
-    const int qgroups = (max_len + 63) / 64;
+    // bf16: two 16-query tiles per wave, 128 queries per workgroup; fp32
+    // (register-heavy): one tile per wave, 64 queries
+    constexpr int QT = sizeof(T) == 2 ? 2 : 1;
+    constexpr int QB = sizeof(T) == 2 ? kTQB : 64;
+    const int qgroups = (max_len + QB - 1) / QB;
     // two query heads of one KV head per workgroup when the group size is even
     const int hpw = (hq / hkv) % 2 == 0 ? 2 : 1;
     const int64_t blocks = (int64_t)n_prompts * (hq / hpw) * qgroups;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    // bf16: two 16-query tiles per wave; fp32 (register-heavy): one
-    constexpr int QT = sizeof(T) == 2 ? 2 : 1;
     if (hpw == 2)
-        thinker_attention_kernel<T, 2, QT><<<(unsigned)blocks, 128 * (4 / QT), 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
+        thinker_attention_kernel<T, 2, QT, QB><<<(unsigned)blocks, 2 * QB / QT * 4, 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
     else
-        thinker_attention_kernel<T, 1, QT><<<(unsigned)blocks, 64 * (4 / QT), 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
+        thinker_attention_kernel<T, 1, QT, QB><<<(unsigned)blocks, QB / QT * 4, 0, s>>>(qkv, cu, hq, hkv, qgroups, out);
     return hipGetLastError();
 }
 
