@@ -44,22 +44,32 @@ __global__ __launch_bounds__(256) void embed_splice_kernel(const T* __restrict__
 }
 
 // ---------------------------------------------------------------- RMSNorm
-// out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g, one wave per row (H <= 4096:
-// up to 16 float4 per lane), persistent over rows.
+// out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g, one wave per row (a row of
+// H <= 256 NQ values is NQ float4 per lane).  The grid normally covers every
+// row at once (each wave walks rows row0, row0 + stride, ... past that); the
+// gain is loaded once per wave, with the first row.
 constexpr int kRmsMaxVec = 16;
 
-template <typename T>
+template <typename T, int NQ>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int M, int H,
                                                       const float* __restrict__ g, float eps, T* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int h4 = H >> 2;
     const float4* g4 = reinterpret_cast<const float4*>(g);
-    for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < M; row += gridDim.x * 4) {
+    int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    float4 gg[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int i = lane + 64 * q;
+        if (i < h4) gg[q] = g4[i];
+    }
+    for (; row < M; row += gridDim.x * 4) {
         const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * H);
-        float4 v[kRmsMaxVec];
+        float4 v[NQ];
         float ss = 0.f;
 #pragma unroll
-        for (int q = 0; q < kRmsMaxVec; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int i = lane + 64 * q;
             if (i < h4) {
                 v[q] = xr[i];
@@ -69,12 +79,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
         const float r = rsqrtf(wsum(ss) / (float)H + eps);
         T* orow = out + (size_t)row * H;
 #pragma unroll
-        for (int q = 0; q < kRmsMaxVec; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int i = lane + 64 * q;
-            if (i < h4) {
-                const float4 gg = g4[i];
-                store4(orow + 4 * i, v[q].x * r * gg.x, v[q].y * r * gg.y, v[q].z * r * gg.z, v[q].w * r * gg.w);
-            }
+            if (i < h4)
+                store4(orow + 4 * i, v[q].x * r * gg[q].x, v[q].y * r * gg[q].y, v[q].z * r * gg[q].z,
+                       v[q].w * r * gg[q].w);
         }
     }
 }
@@ -85,24 +94,53 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 // [128] gain, then the rotate-half RoPE at the token's position:
 // (a, b) = (x[i], x[i + 64]) -> (a c - b s, b c + a s), c, s = cos, sin of
 // pos * base^(-i / 64), taken from a table computed in double on the host.
-// One wave per (token, head); lane i holds the pair (i, i + 64).
+// 16 lanes per (token, head), 4 per wave: lane j of a group holds the pairs
+// (i, i + 64) for i = 4 j .. 4 j + 3, read and written as 4-element vectors.
+__device__ __forceinline__ void load4f(const float* p, float* v) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void load4f(const bf16* p, float* v) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
+    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* __restrict__ qkv, int M, int hq, int hkv,
                                                           const int* __restrict__ pos,
                                                           const float* __restrict__ qg, const float* __restrict__ kg,
                                                           const float2* __restrict__ cs, float eps) {
-    const int item = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, j = lane & 15;
+    const int64_t item = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
     const int heads = hq + hkv;
-    if (item >= M * heads) return;
-    const int t = item / heads, h = item - t * heads;
-    T* p = qkv + (size_t)t * (hq + 2 * hkv) * 128 + h * 128;
-    const float a = to_f32(p[lane]), b = to_f32(p[lane + 64]);
-    const float r = rsqrtf(wsum(a * a + b * b) / 128.0f + eps);
-    const float* gg = h < hq ? qg : kg;
-    const float an = a * r * gg[lane], bn = b * r * gg[lane + 64];
-    const float2 c = cs[(size_t)pos[t] * 64 + lane];
-    p[lane] = from_f32<T>(an * c.x - bn * c.y);
-    p[lane + 64] = from_f32<T>(bn * c.x + an * c.y);
+    if (item >= (int64_t)M * heads) return;              // uniform within the 16-lane group
+    const int t = (int)(item / heads), h = (int)(item - (int64_t)t * heads);
+    T* p = qkv + (size_t)t * (hq + 2 * hkv) * 128 + h * 128 + 4 * j;
+    float a[4], b[4];
+    load4f(p, a);
+    load4f(p + 64, b);
+    const float* gp = (h < hq ? qg : kg) + 4 * j;
+    const float4 ga = *reinterpret_cast<const float4*>(gp), gb = *reinterpret_cast<const float4*>(gp + 64);
+    const float4* c4 = reinterpret_cast<const float4*>(cs + (size_t)pos[t] * 64 + 4 * j);
+    const float4 c01 = c4[0], c23 = c4[1];                // (cos, sin) of i = 4 j .. 4 j + 3
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + b[e] * b[e];
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float r = rsqrtf(ss / 128.0f + eps);
+    const float gA[4] = {ga.x, ga.y, ga.z, ga.w}, gB[4] = {gb.x, gb.y, gb.z, gb.w};
+    const float cc[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+    float oa[4], ob[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float an = a[e] * r * gA[e], bn = b[e] * r * gB[e];
+        oa[e] = an * cc[e] - bn * sn[e];
+        ob[e] = bn * cc[e] + an * sn[e];
+    }
+    store4(p, oa[0], oa[1], oa[2], oa[3]);
+    store4(p + 64, ob[0], ob[1], ob[2], ob[3]);
 }
 
 // ---------------------------------------------------------------- attention
@@ -417,8 +455,10 @@ template <typename T>
 hipError_t rmsnorm(hipStream_t s, const float* x, int M, int H, const float* g, float eps, T* out) {
     if (M <= 0) return hipSuccess;
     if (H % 4 || H > 4 * 64 * kRmsMaxVec) return hipErrorInvalidValue;
-    const int blocks = min((M + 3) / 4, 1024);
-    rmsnorm_kernel<T><<<blocks, 256, 0, s>>>(x, M, H, g, eps, out);
+    const int blocks = min((M + 3) / 4, 16384);             // one wave per row up to 64K rows
+    if (H <= 1024) rmsnorm_kernel<T, 4><<<blocks, 256, 0, s>>>(x, M, H, g, eps, out);
+    else if (H <= 2048) rmsnorm_kernel<T, 8><<<blocks, 256, 0, s>>>(x, M, H, g, eps, out);
+    else rmsnorm_kernel<T, kRmsMaxVec><<<blocks, 256, 0, s>>>(x, M, H, g, eps, out);
     return hipGetLastError();
 }
 
@@ -426,8 +466,9 @@ template <typename T>
 hipError_t qknorm_rope(hipStream_t s, T* qkv, int M, int hq, int hkv, const int* pos, const float* qg,
                        const float* kg, const float2* cs, float eps) {
     if (M <= 0) return hipSuccess;
-    const int64_t items = (int64_t)M * (hq + hkv);
-    qknorm_rope_kernel<T><<<(unsigned)((items + 3) / 4), 256, 0, s>>>(qkv, M, hq, hkv, pos, qg, kg, cs, eps);
+    const int64_t items = (int64_t)M * (hq + hkv);          // 16 per workgroup (4 per wave)
+    if ((items + 15) / 16 > 0x7fffffff) return hipErrorInvalidValue;
+    qknorm_rope_kernel<T><<<(unsigned)((items + 15) / 16), 256, 0, s>>>(qkv, M, hq, hkv, pos, qg, kg, cs, eps);
     return hipGetLastError();
 }
 
