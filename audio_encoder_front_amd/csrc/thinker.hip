@@ -158,10 +158,23 @@ constexpr int kTHd = 128;
 constexpr int kTKB = 64;                     // keys per block
 constexpr int kTQB = 128;                    // queries per workgroup (bf16)
 
+// bf16: LDS row of key k within its 32-key step.  The S^T MFMA gives lane
+// group g the rows 4 g .. 4 g + 3 of each 16-row tile; storing key
+// 8 g + 4 h + r at row 16 h + 4 g + r makes the 8 probabilities a lane feeds
+// to the P.V MFMA those of 8 consecutive keys, so their V^T values are one
+// 16-byte read.
+__device__ __forceinline__ int tkey_row(int k) {
+    return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+}
+// The inverse: the key held at LDS row rho.
+__device__ __forceinline__ int trow_key(int rho) {
+    return (rho & ~31) | (((rho >> 2) & 3) << 3) | (((rho >> 4) & 1) << 2) | (rho & 3);
+}
+
 template <typename T> struct TAttnLds;
 template <> struct TAttnLds<bf16> {
     static constexpr int krow = kTHd * 2 + 16;      // bytes per K row (padded)
-    static constexpr int vrow = kTKB * 2 + 24;      // bytes per V^T row (row vt_row(d) for dim d)
+    static constexpr int vrow = kTKB * 2 + 16;      // bytes per V^T row (row vt_row(d) for dim d; 16-byte reads)
 };
 template <> struct TAttnLds<float> {
     static constexpr int krow = kTHd * 4 + 16;
@@ -177,7 +190,8 @@ template <> struct TAttnLds<float> {
 template <int QT>
 __device__ __forceinline__ void tpv_step(bf16, const char* vt, int kbase, int fr, int fg,
                                          const f32x4 (*p)[kTKB / 16], int t0, f32x4 (*o)[kTHd / 16 + 1]) {
-    // slots 0..3: keys kbase + 4g + r (tile t0), 4..7: kbase + 16 + 4g + r (tile t0 + 1)
+    // slots 0..3: LDS rows kbase + 4g + r (tile t0), 4..7: kbase + 16 + 4g + r
+    // (tile t0 + 1), i.e. keys kbase + 8 g .. kbase + 8 g + 7 (tkey_row)
     bf16x8 pb[QT];
 #pragma unroll
     for (int u = 0; u < QT; ++u)
@@ -191,9 +205,7 @@ __device__ __forceinline__ void tpv_step(bf16, const char* vt, int kbase, int fr
 #pragma unroll
     for (int dt = 0; dt < kTHd / 16; ++dt) {
         const char* row = vt + vt_row(dt * 16 + fr) * TAttnLds<bf16>::vrow;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 4 * fg));
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 2 * (kbase + 16 + 4 * fg));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, ld16(row + 2 * (kbase + 8 * fg)));
 #pragma unroll
         for (int u = 0; u < QT; ++u) o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[u], o[u][dt], 0, 0, 0);
     }
@@ -313,7 +325,8 @@ __global__ __launch_bounds__(HPW * QB / QT * 4) __attribute__((amdgpu_waves_per_
         {
             const int ch = tid % CPR;
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) st16(ks + key_of(c) * KR + ch * 16, kv[c]);
+            for (int c = 0; c < NCH; ++c)
+                st16(ks + (sizeof(T) == 2 ? tkey_row(key_of(c)) : key_of(c)) * KR + ch * 16, kv[c]);
             if constexpr (sizeof(T) == 2) {
 #pragma unroll
                 for (int c = 0; c < NCH; c += 2) {
@@ -356,7 +369,8 @@ __global__ __launch_bounds__(HPW * QB / QT * 4) __attribute__((amdgpu_waves_per_
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // lane holds S^T[key k0 + 16 kt + 4 fg + r][query (qt0 + u) 16 + fr] (unscaled)
+        // lane holds S^T[LDS row 16 kt + 4 fg + r][query (qt0 + u) 16 + fr] (unscaled);
+        // the row is key k0 + trow_key(row) in bf16, key k0 + row in fp32
         const bool full = k0 + kTKB - 1 <= qt0 * 16 && k0 + kTKB <= n;   // visible to every query of the wave
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
@@ -372,7 +386,8 @@ __global__ __launch_bounds__(HPW * QB / QT * 4) __attribute__((amdgpu_waves_per_
                 for (int kt = 0; kt < kTKB / 16; ++kt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int key = k0 + kt * 16 + 4 * fg + r;
+                        const int rho = kt * 16 + 4 * fg + r;
+                        const int key = k0 + (sizeof(T) == 2 ? trow_key(rho) : rho);
                         const float v = (key <= q && key < n) ? sacc[u][kt][r] : -INFINITY;
                         sacc[u][kt][r] = v;
                         bm = fmaxf(bm, v);
