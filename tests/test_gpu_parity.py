@@ -173,3 +173,21 @@ def test_b17_packed_16_clips_sampled_windows(b17):
     rep = compare(wl.dims, w, clips, out, taps,
                   windows_per_clip=lambda ci, nw: range(nw) if ci == shortest else [0, nw - 1])
     _print("b17_16", rep)
+
+
+@pytest.mark.parametrize("base,window_chunks", [("tiny", 9), ("tiny", 1), ("b06", 9)])
+def test_other_window_sizes(base, window_chunks):
+    """Attention windows of 9 chunks (117 tokens: the 8-key-tile kernel, whose
+    last P.V step is a full 32-key step) and of 1 chunk (13 tokens: mostly
+    masked key tiles), fp32 miniature and 0.6B bf16."""
+    import dataclasses
+    dims = dataclasses.replace(synth.DIMS_TINY if base == "tiny" else synth.DIMS_06B, window_chunks=window_chunks)
+    w = synth.make_weights(dims, 110 + window_chunks)
+    enc = make_encoder(dims, w)
+    lens = [480000, 12 * 16000 + 77, 16000 * 9 + 160 * 40]
+    clips = [synth.speech_like_clip(n, [93, i]) for i, n in enumerate(lens)]
+    _print(f"case: {base} {dims.dtype}, {window_chunks}-chunk windows", lens)
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(dims, w, clips, out, taps)
+    _print(f"{base} window {window_chunks}", rep)
+    enc.free()
