@@ -191,3 +191,20 @@ def test_other_window_sizes(base, window_chunks):
     rep = compare(dims, w, clips, out, taps)
     _print(f"{base} window {window_chunks}", rep)
     enc.free()
+
+
+def test_bf16_wide_stem_valu_conv1():
+    """bf16 with 544 stem channels (> 512): conv1 takes the VALU kernel with an
+    NHWC output and conv2 gathers NHWC input instead of the channel-blocked
+    layout of the MFMA conv1."""
+    import dataclasses
+    dims = dataclasses.replace(synth.DIMS_TINY, conv_channels=544, dtype="bf16")
+    w = synth.make_weights(dims, 120)
+    enc = make_encoder(dims, w)
+    lens = [16000 * 10 + 160 * 37 + 11, 16000 * 2]
+    clips = [synth.speech_like_clip(n, [94, i]) for i, n in enumerate(lens)]
+    _print("case: tiny bf16, 544 stem channels", lens)
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(dims, w, clips, out, taps)
+    _print("wide stem", rep)
+    enc.free()

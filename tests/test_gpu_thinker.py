@@ -120,6 +120,18 @@ def test_bf16_thinker_shapes(dims, seed, spec):
     print("bf16 thinker worst (hidden, logits)", _check(dims, W, prompts, audio, hid, lg), flush=True)
 
 
+def test_tiny_thinker_odd_gqa_group():
+    """fp32, 3 query heads per KV head: one query head per attention workgroup."""
+    d = ST.ThinkerDims(hidden=256, n_layers=2, n_q_heads=3, n_kv_heads=1, ffn_dim=256, vocab=1000, dtype="f32")
+    W = ST.make_weights(d, 250)
+    prompts = _prompts([150, 3], d.vocab, 251)
+    n_audio = sum(p[2] for p in prompts)
+    audio = ST.make_audio_states(n_audio, d.hidden, [252, 0])
+    print("case: tiny thinker, 3/1 heads", [len(p[0]) for p in prompts], flush=True)
+    hid, lg = _run(d, W, prompts, audio)
+    print("odd-group thinker worst (hidden, logits)", _check(d, W, prompts, audio, hid, lg), flush=True)
+
+
 def test_tiny_thinker_ragged_widths():
     """Widths that leave partial 16-byte chunks in the GEMM epilogues: a vocab
     of 1003 (the fp32 logits rows end 3 values into a chunk) and an FFN of 48
