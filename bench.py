@@ -209,7 +209,7 @@ def main():
                     help="also run one 1 GiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the encoder runs on a single MI355X and this build has no "
+        print(f"bench.py measures one GPU: the encoder runs on a single MI355X and the library has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
