@@ -14,9 +14,13 @@
 // samples contribute, i.e. taps p + j up with p = (n down + half) mod up, so
 // output n is a dot product of one table row hp[p][0..L) (L = ceil(taps / up),
 // zero padded) with the input samples q, q - 1, ..., q = (n down + half) / up.
-// The work is bound by HBM (4 bytes read per input sample, 4 written per
-// output sample) once the input is staged in LDS and the taps run as four
-// independent FMA chains.
+// Each output reads its L taps and L samples from LDS, so the kernel is bound
+// by LDS reads, not by HBM (4 bytes read per input sample, 4 written per
+// output sample).  Neighbouring outputs use different table rows; the LDS
+// copy of the table has a row stride of 4 x (an odd number) floats, so the
+// 16-byte tap reads of 16 lanes land in 16 different bank groups whenever
+// their phases differ modulo 16 (for 44.1 kHz the phase steps by 121 of 160
+// per output).
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -39,55 +43,79 @@ constexpr int kResampleHalfFactor = 10;
 
 constexpr int kResampleThreads = 256;
 constexpr int kResampleMaxWindow = 16384;      // staged input samples per workgroup (64 KB of LDS)
-constexpr int kResampleMaxLdsTable = 12288;    // tables up to 48 KB are staged in LDS too
+constexpr int kResampleMaxLdsTable = 12288;    // tables up to 48 KB (padded rows) are staged in LDS too
 
-// A workgroup computes opb = 256 OPT consecutive outputs.  The input samples
-// they read are staged once in LDS (zeros outside the clip, so the taps need
-// no bounds checks); each thread then forms its OPT outputs as dot products of
-// one table row (L taps, a multiple of 4, zero padded; read as float4) with
-// the staged samples, in four partial sums.
+// LDS row stride of the table: L (a multiple of 4) rounded up to 4 x an odd number.
+__host__ __device__ constexpr int resample_lds_row(int L) { return (L / 4) % 2 ? L : L + 4; }
+
+// A block of opb = 256 OPT consecutive outputs reads a contiguous input
+// window; each thread forms OPT of them as dot products of one table row (L
+// taps, a multiple of 4, zero padded; read as float4) with the window staged
+// in LDS (zeros outside the clip, so the taps need no bounds checks), in four
+// partial sums.  The grid is persistent: a workgroup stages the table once
+// and then walks the output blocks blockIdx.x, blockIdx.x + gridDim.x, ...
 template <int OPT, bool TLDS>
 __global__ __launch_bounds__(kResampleThreads) void resample_kernel(const float* __restrict__ x, int64_t n_in,
                                                                     float* __restrict__ y, int64_t n_out,
                                                                     const float* __restrict__ hp, int up, int down,
-                                                                    int half, int L) {
+                                                                    int half, int L, int64_t n_blocks) {
     extern __shared__ float xs[];
     constexpr int opb = kResampleThreads * OPT;
-    const int64_t n0 = blockIdx.x * (int64_t)opb;
-    const int64_t n_last = (n0 + opb < n_out ? n0 + opb : n_out) - 1;
-    const int64_t lo = (n0 * down + half) / up - (L - 1);           // lowest input sample read
-    const int cnt = (int)((n_last * down + half) / up - lo + 1);   // <= kResampleMaxWindow (host-checked)
-    // table first (16-byte aligned at the start of LDS), then the window
+    // table first (16-byte aligned at the start of LDS, rows of LT floats),
+    // then the window
+    const int LT = resample_lds_row(L);
     float* tab = xs;
-    float* win = TLDS ? xs + up * L : xs;
+    float* win = TLDS ? xs + up * LT : xs;
     if (TLDS) {
         const float4* src = reinterpret_cast<const float4*>(hp);
         float4* dst = reinterpret_cast<float4*>(tab);
-        for (int i = threadIdx.x; i < up * L / 4; i += kResampleThreads) dst[i] = src[i];
-    }
-    for (int i = threadIdx.x; i < cnt; i += kResampleThreads) {
-        const int64_t g = lo + i;
-        win[i] = g >= 0 && g < n_in ? x[g] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < OPT; ++k) {
-        const int64_t n = n0 + threadIdx.x + k * kResampleThreads;
-        if (n > n_last) break;
-        const int64_t t = n * down + half;          // upsampled index met by tap 0
-        const int p = (int)(t % up);
-        const int qs = (int)(t / up - lo);           // staged index of input sample q = t / up
-        const float4* hr = reinterpret_cast<const float4*>((TLDS ? tab : hp) + (size_t)p * L);
-        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-        for (int j4 = 0; j4 < L / 4; ++j4) {         // tap p + j up meets sample q - j
-            const float4 h = hr[j4];
-            const int b = qs - 4 * j4;
-            a0 = fmaf(h.x, win[b], a0);
-            a1 = fmaf(h.y, win[b - 1], a1);
-            a2 = fmaf(h.z, win[b - 2], a2);
-            a3 = fmaf(h.w, win[b - 3], a3);
+        for (int i = threadIdx.x; i < up * L / 4; i += kResampleThreads) {
+            const int row = i / (L / 4), c = i - row * (L / 4);
+            dst[row * (LT / 4) + c] = src[i];
         }
-        y[n] = (a0 + a1) + (a2 + a3);
+    }
+    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+        const int64_t n0 = blk * opb;
+        const int64_t n_last = (n0 + opb < n_out ? n0 + opb : n_out) - 1;
+        const int64_t lo = (n0 * down + half) / up - (L - 1);           // lowest input sample read
+        const int cnt = (int)((n_last * down + half) / up - lo + 1);   // <= kResampleMaxWindow (host-checked)
+        __syncthreads();                                                // previous window consumed
+        // eight loads in flight per thread before their LDS stores
+        for (int i0 = 0; i0 < cnt; i0 += 8 * kResampleThreads) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kResampleThreads + threadIdx.x;
+                const int64_t g = lo + i;
+                v[u] = i < cnt && g >= 0 && g < n_in ? x[g] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kResampleThreads + threadIdx.x;
+                if (i < cnt) win[i] = v[u];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < OPT; ++k) {
+            const int64_t n = n0 + threadIdx.x + k * kResampleThreads;
+            if (n > n_last) break;
+            const int64_t t = n * down + half;          // upsampled index met by tap 0
+            const int p = (int)(t % up);
+            const int qs = (int)(t / up - lo);           // staged index of input sample q = t / up
+            const float4* hr =
+                reinterpret_cast<const float4*>(TLDS ? tab + (size_t)p * LT : hp + (size_t)p * L);
+            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+            for (int j4 = 0; j4 < L / 4; ++j4) {         // tap p + j up meets sample q - j
+                const float4 h = hr[j4];
+                const int b = qs - 4 * j4;
+                a0 = fmaf(h.x, win[b], a0);
+                a1 = fmaf(h.y, win[b - 1], a1);
+                a2 = fmaf(h.z, win[b - 2], a2);
+                a3 = fmaf(h.w, win[b - 3], a3);
+            }
+            y[n] = (a0 + a1) + (a2 + a3);
+        }
     }
 }
 
@@ -183,12 +211,18 @@ QA_API int qa_resample(qa_resampler* r, void* hip_stream, const float* in, int64
     }
     const int64_t opb = (int64_t)qa::kResampleThreads * opt;
     const int64_t blocks = (n_out + opb - 1) / opb;
-    if (blocks > 0x7fffffff) { qa::set_error_message("qa_resample: input too long"); return QA_STATUS_INVALID_PARAMS; }
-    const bool tlds = (int64_t)r->up * r->L <= qa::kResampleMaxLdsTable;
-    const size_t lds = ((size_t)window(qa::kResampleThreads * opt) + (tlds ? (size_t)r->up * r->L : 0)) * sizeof(float);
+    const int64_t lt = (int64_t)r->up * qa::resample_lds_row(r->L);
+    const bool tlds = lt <= qa::kResampleMaxLdsTable;
+    const size_t lds = ((size_t)window(qa::kResampleThreads * opt) + (tlds ? (size_t)lt : 0)) * sizeof(float);
+    // persistent grid: a few workgroups per CU (as many as the LDS allows, at
+    // most 4), each staging the table once
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int per_cu = std::max(1, std::min(4, (int)(160 * 1024 / std::max<size_t>(lds, 1))));
+    const unsigned grid = (unsigned)std::min<int64_t>(blocks, (int64_t)cus * per_cu);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-#define QA_RS(o, t) qa::resample_kernel<o, t><<<(unsigned)blocks, qa::kResampleThreads, lds, s>>>( \
-        in, n_in, out, n_out, r->table, r->up, r->down, r->half, r->L)
+#define QA_RS(o, t) qa::resample_kernel<o, t><<<grid, qa::kResampleThreads, lds, s>>>( \
+        in, n_in, out, n_out, r->table, r->up, r->down, r->half, r->L, blocks)
     if (tlds) {
         if (opt == 4) QA_RS(4, true); else if (opt == 2) QA_RS(2, true); else QA_RS(1, true);
     } else {
