@@ -36,7 +36,7 @@ def plan_counts(lengths, chunk_tok=13, window_chunks=8):
         chunks += full + (1 if tail else 0)
         t = full * chunk_tok + ((tail + 7) // 8 if tail else 0)
         tokens += t
-        w = chunk_tok * window_chunks
+        w = chunk_tok * window_chunks if window_chunks else max(t, 1)   # 0: one segment per clip
         windows += [min(w, t - s) for s in range(0, t, w)]
     return chunks, tokens, frames, windows
 
@@ -175,6 +175,51 @@ def thinker_bench(dev, enc_out, wl, reps: int = 3):
             "mfma_frac": round(flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)}
 
 
+def full_input_bench(dev, wl, weights, n_clips: int = 40, seconds: int = 30, steps: int = 5):
+    """Full-input attention (one attention segment per clip, the variant for
+    bounded inputs of at most 30 s), timed on its own (not part of `value`):
+    the same encoder and weights with window_chunks = 0 on n_clips clips of
+    `seconds` each (the same audio duration as the 20-minute workload)."""
+    import dataclasses
+    import numpy as np
+    import torch
+    import audio_encoder_front_amd as qa
+    import synth
+    dims = dataclasses.replace(wl.dims, window_chunks=0)
+    enc = qa.qa_encoder_create(weights, dims)
+    stream = torch.cuda.current_stream(dev)
+    qa.qa_encoder_set_stream(enc, stream)
+    clips = [synth.speech_like_clip(seconds * 16000, [wl.audio_seed + 1000, i]) for i in range(n_clips)]
+    lengths = [len(c) for c in clips]
+    pcm = torch.from_numpy(np.concatenate(clips)).to(dev)
+    T = sum(qa.qa_encode_num_tokens(n) for n in lengths)
+    out = torch.empty((T, dims.output_dim), dtype=torch.float32, device=dev)
+    qa.qa_encode(enc, pcm, lengths, out)
+    qa.qa_encoder_set_profiling(enc, True)
+    qa.qa_encode(enc, pcm, lengths, out)
+    torch.cuda.synchronize()
+    times = qa.qa_encoder_kernel_times(enc)
+    qa.qa_encoder_set_profiling(enc, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        qa.qa_encode(enc, pcm, lengths, out)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    enc.free()
+    work, (_, _, _, segs) = kernel_work(dims, lengths)
+    att_ms, att_n = times["attention"]
+    att_avg = att_ms / max(att_n, 1)
+    f, b, _ = work["attention"]
+    return {"workload": f"{n_clips} clips x {seconds} s, one attention segment per clip "
+                        f"({max(segs)} tokens), same encoder and weights",
+            "audio_s_per_s": round(n_clips * seconds / dt, 1), "ms_per_step": round(dt * 1e3, 3),
+            "attention": {"avg_ms": round(att_avg, 5), "launches": int(att_n),
+                          "tflops": round(f / (att_avg * 1e-3) / 1e12, 1),
+                          "frac_of_bf16_peak": round(f / (att_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "gbs": round(b / (att_avg * 1e-3) / 1e9, 1)}}
+
+
 def cpu_baseline(wl, seconds: float):
     """The fp64 oracle on the first `seconds` of the workload's first clip."""
     import numpy as np
@@ -205,6 +250,7 @@ def main():
     ap.add_argument("--cpu-sample-s", type=float, default=240.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-thinker", action="store_true", help="skip the Thinker-prefill line")
+    ap.add_argument("--no-full-input", action="store_true", help="skip the full-input attention line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -225,7 +271,6 @@ def main():
     dev = torch.device("cuda:0")
     pcm = torch.from_numpy(np.concatenate(clips)).to(dev)
     enc = qa.qa_encoder_create(weights, wl.dims)
-    del weights
     stream = torch.cuda.current_stream(dev)
     qa.qa_encoder_set_stream(enc, stream)
     total_tok = sum(qa.qa_encode_num_tokens(n) for n in lengths)
@@ -307,6 +352,9 @@ def main():
                         "the timed steps carry events only around the dominant kernel",
     }
     res["resample"] = resample_bench(dev)
+    if not args.no_full_input and wl.dims.window_chunks:
+        res["full_input"] = full_input_bench(dev, wl, weights)
+    del weights
     if not args.no_thinker:
         res["thinker_prefill"] = thinker_bench(dev, out, wl)
     if args.calibrate_copy:
