@@ -317,132 +317,270 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 }
 
 // Segments longer than 128 tokens (full-input attention over a whole clip):
-// one workgroup per (segment, head, group of 64 queries), one 16-query tile
-// per wave; keys stream through LDS in blocks of 128 with an online softmax
-// (running max and sum per query, the partial output rescaled when the max
-// grows).  Same MFMA layouts as the windowed kernel.
-template <typename T>
-__global__ __launch_bounds__(256) void attention_long_kernel(const T* __restrict__ qkv, const int* __restrict__ cu,
-                                                             int n_heads, int d, int qgroups, T* __restrict__ out) {
-    constexpr int QR = AttnLds<T, kMaxWindow>::qrow, VR = AttnLds<T, kMaxWindow>::vrow;
+// one workgroup per (segment, head, block of QB queries): 128 queries in bf16
+// with two 16-query tiles per wave (each K / V fragment read from LDS feeds
+// two MFMAs), 64 in fp32 with one.  Keys stream through LDS in blocks of 64,
+// loaded into registers two blocks ahead (two register sets alternate), with
+// an online softmax in log2 units: the 1/sqrt(64) scale folded into the exp2
+// argument, and the reference maximum moved (and the partial output
+// rescaled) only when some lane's block maximum exceeds it by more than
+// kLazy, so the probabilities stay below 2^kLazy.  bf16: V goes to LDS
+// transposed as key pairs (one 4-byte write per two keys of a dimension),
+// the K rows of each 32-key step sit permuted (key 8 g + 4 h + r at row
+// 16 h + 4 g + r) so that the 8 probabilities a lane feeds to the P.V MFMA
+// are 8 consecutive keys and their V^T values one 16-byte read, and the row
+// sums come from one more MFMA against an all-ones operand (the same
+// bf16-rounded probabilities that weight V).
+constexpr int kLKB = 64;                         // keys per block
+constexpr float kLazy = 8.f;
+
+__device__ __forceinline__ int lkey_row(int k) {   // LDS row of key k (bf16)
+    return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+}
+__device__ __forceinline__ int lrow_key(int rho) { // key held at LDS row rho (bf16)
+    return (rho & ~31) | (((rho >> 2) & 3) << 3) | (((rho >> 4) & 1) << 2) | (rho & 3);
+}
+
+template <typename T> struct LAttnLds;
+template <> struct LAttnLds<bf16> {
+    static constexpr int krow = kHd * 2 + 16;
+    static constexpr int vrow = kLKB * 2 + 16;   // 16-byte V^T reads
+};
+template <> struct LAttnLds<float> {
+    static constexpr int krow = kHd * 4 + 16;
+    static constexpr int vrow = kLKB * 4 + 16;
+};
+
+template <int QT, int VR>
+__device__ __forceinline__ void lpv_step(bf16, const char* vt, int kbase, int fr, int fg,
+                                         const f32x4 (*p)[kLKB / 16], int t0, f32x4 (*o)[kHd / 16 + 1]) {
+    // slots 0..3: LDS rows kbase + 4 g + r, 4..7: kbase + 16 + 4 g + r, i.e.
+    // keys kbase + 8 g .. + 7
+    bf16x8 pb[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { pb[u][r] = (bf16)p[u][t0][r]; pb[u][4 + r] = (bf16)p[u][t0 + 1][r]; }
+    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);   // bf16 1.0 x 8
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+        o[u][kHd / 16] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), pb[u], o[u][kHd / 16], 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < kHd / 16; ++dt) {
+        const bf16x8 va = __builtin_bit_cast(bf16x8, ld16(vt + vt_row(dt * 16 + fr) * VR + 2 * (kbase + 8 * fg)));
+#pragma unroll
+        for (int u = 0; u < QT; ++u) o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[u], o[u][dt], 0, 0, 0);
+    }
+}
+template <int QT, int VR>
+__device__ __forceinline__ void lpv_step(float, const char* vt, int kbase, int fr, int fg,
+                                         const f32x4 (*p)[kLKB / 16], int t0, f32x4 (*o)[kHd / 16 + 1]) {
+#pragma unroll
+    for (int dt = 0; dt < kHd / 16; ++dt) {
+        const float4 va = *reinterpret_cast<const float4*>(vt + vt_row(dt * 16 + fr) * VR + 4 * (kbase + 4 * fg));
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+            o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, p[u][t0][0], o[u][dt], 0, 0, 0);
+            o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, p[u][t0][1], o[u][dt], 0, 0, 0);
+            o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, p[u][t0][2], o[u][dt], 0, 0, 0);
+            o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, p[u][t0][3], o[u][dt], 0, 0, 0);
+        }
+    }
+}
+
+template <typename T, int QT, int QB>
+__global__ __launch_bounds__(QB / QT * 4) __attribute__((amdgpu_waves_per_eu(2))) void attention_long_kernel(
+    const T* __restrict__ qkv, const int* __restrict__ cu, int n_heads, int d, int qgroups, T* __restrict__ out) {
+    constexpr bool kB = sizeof(T) == 2;
+    constexpr int KR = LAttnLds<T>::krow, VR = LAttnLds<T>::vrow;
     constexpr int PER = Elem<T>::per16;
-    constexpr int CPR = kHd / PER;
-    constexpr int KBN = kHd * (int)sizeof(T) / 64;
-    constexpr int NCH = kMaxWindow * CPR / 256;
-    __shared__ __align__(16) char ks[kMaxWindow * QR];
+    constexpr int CPR = kHd / PER;                   // 16-byte chunks per head row
+    constexpr int KBN = kHd * (int)sizeof(T) / 64;   // 64-byte MFMA K blocks per head row
+    constexpr int NW = QB / 16 / QT, NT = 64 * NW;
+    constexpr int NCH = kLKB * CPR / NT;             // chunks per thread per key block
+    static_assert(QB % (16 * QT) == 0 && (kLKB * CPR) % NT == 0 && (!kB || NCH % 2 == 0), "tiling");
+    __shared__ __align__(16) char ks[kLKB * KR];
     __shared__ __align__(16) char vts[kHd * VR];
 
     const int qg = blockIdx.x % qgroups;
     const int sh = blockIdx.x / qgroups;
     const int seg = sh / n_heads, h = sh % n_heads;
     const int s0 = cu[seg], n = cu[seg + 1] - s0;
-    if (qg * 64 >= n) return;                       // whole workgroup idle (uniform)
+    if (qg * QB >= n) return;                        // whole workgroup idle (uniform)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int fr = lane & 15, fg = lane >> 4;
     const size_t ld = 3 * (size_t)d;
-    const int qt = qg * 4 + wave;
-    const bool active = qt * 16 < n;                // wave-uniform
-    uint4 qf[KBN];
-    {
-        const int q = qt * 16 + fr;
+    const T* kbase_p = qkv + (size_t)s0 * ld + d + h * kHd;
+    const T* vbase_p = kbase_p + d;
+    const int qt0 = qg * (QB / 16) + wave * QT;      // this wave's first query tile
+    const bool active = qt0 * 16 < n;                // wave-uniform
+    uint4 qf[QT][KBN];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+        const int q = qt0 * 16 + u * 16 + fr;
         const T* row = qkv + (size_t)(s0 + q) * ld + h * kHd + fg * PER;
 #pragma unroll
-        for (int kb = 0; kb < KBN; ++kb) qf[kb] = q < n ? ld16(row + kb * (64 / (int)sizeof(T))) : zero16();
+        for (int kb = 0; kb < KBN; ++kb) qf[u][kb] = q < n ? ld16(row + kb * (64 / (int)sizeof(T))) : zero16();
     }
-    const float sc = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
-    float m = -INFINITY, l = 0.f;
-    f32x4 o[4];
+    const float sc = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
+    float m[QT], l[QT];
+    f32x4 o[QT][kHd / 16 + 1];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < n; k0 += kMaxWindow) {
-        __syncthreads();                            // previous key block consumed
-        uint4 kv[NCH], vv[NCH];
+    for (int u = 0; u < QT; ++u) {
+        m[u] = -INFINITY;
+        l[u] = 0.f;
 #pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            const int idx = tid + q * 256;
-            const int t = idx / CPR, c = idx % CPR;
-            kv[q] = vv[q] = zero16();
+        for (int dt = 0; dt <= kHd / 16; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // chunk c of this thread: key row key_of(c), 16-byte column tid % CPR;
+    // bf16 keys come in adjacent pairs (2 p, 2 p + 1)
+    auto key_of = [&](int c) {
+        if constexpr (kB) return 2 * (tid / CPR + (c / 2) * (NT / CPR)) + (c & 1);
+        else return (tid + c * NT) / CPR;
+    };
+    using Regs = uint4[NCH];
+    Regs kvA, vvA, kvB, vvB;
+    auto load_block = [&](int k0, Regs& kv, Regs& vv) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int t = key_of(c), ch = tid % CPR;
+            kv[c] = vv[c] = zero16();
             if (k0 + t < n) {
-                const T* row = qkv + (size_t)(s0 + k0 + t) * ld + d + h * kHd + c * PER;
-                kv[q] = ld16(row);
-                vv[q] = ld16(row + d);
+                const size_t off = (size_t)(k0 + t) * ld + ch * PER;
+                kv[c] = ld16(kbase_p + off);
+                vv[c] = ld16(vbase_p + off);
             }
         }
+    };
+    auto process = [&](int k0, Regs& kv, Regs& vv) {
+        __syncthreads();                             // previous block consumed
+        {
+            const int ch = tid % CPR;
 #pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            const int idx = tid + q * 256;
-            const int t = idx / CPR, c = idx % CPR;
-            st16(ks + t * QR + c * 16, kv[q]);
-            const T* ve = reinterpret_cast<const T*>(&vv[q]);
+            for (int c = 0; c < NCH; ++c) st16(ks + (kB ? lkey_row(key_of(c)) : key_of(c)) * KR + ch * 16, kv[c]);
+            if constexpr (kB) {
 #pragma unroll
-            for (int e = 0; e < PER; ++e)
-                *reinterpret_cast<T*>(vts + vt_row(c * PER + e) * VR + t * sizeof(T)) = ve[e];
+                for (int c = 0; c < NCH; c += 2) {
+                    const int t = key_of(c);         // even; t + 1 is chunk c + 1's key
+                    const unsigned* va = reinterpret_cast<const unsigned*>(&vv[c]);
+                    const unsigned* vb = reinterpret_cast<const unsigned*>(&vv[c + 1]);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {    // dims 2 w, 2 w + 1 of the chunk
+                        *reinterpret_cast<unsigned*>(vts + vt_row(ch * PER + 2 * w) * VR + t * 2) =
+                            __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);
+                        *reinterpret_cast<unsigned*>(vts + vt_row(ch * PER + 2 * w + 1) * VR + t * 2) =
+                            __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const T* ve = reinterpret_cast<const T*>(&vv[c]);
+#pragma unroll
+                    for (int e = 0; e < PER; ++e)
+                        *reinterpret_cast<T*>(vts + vt_row(ch * PER + e) * VR + key_of(c) * sizeof(T)) = ve[e];
+                }
+            }
         }
         __syncthreads();
-        if (!active) continue;
-        f32x4 sacc[8];
+        if (k0 + 2 * kLKB < n) load_block(k0 + 2 * kLKB, kv, vv);
+        if (!active) return;
+        f32x4 sacc[QT][kLKB / 16];
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < QT; ++u)
+#pragma unroll
+            for (int kt = 0; kt < kLKB / 16; ++kt) sacc[u][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
-                const uint4 kf = ld16(ks + (kt * 16 + fr) * QR + fg * 16 + kb * 64);
-                mfma_kblock(T(), kf, qf[kb], sacc[kt]);
+            for (int kt = 0; kt < kLKB / 16; ++kt) {
+                const uint4 kf = ld16(ks + (kt * 16 + fr) * KR + fg * 16 + kb * 64);
+#pragma unroll
+                for (int u = 0; u < QT; ++u) mfma_kblock(T(), kf, qf[u][kb], sacc[u][kt]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        float bm = -INFINITY;
+        // lane holds S^T[LDS row 16 kt + 4 fg + r][query] (unscaled); the row is
+        // key k0 + lrow_key(row) in bf16, key k0 + row in fp32
+        const bool full = k0 + kLKB <= n;
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
+        for (int u = 0; u < QT; ++u) {
+            float bm = -INFINITY;
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + kt * 16 + 4 * fg + r;
-                const float v = key < n ? sacc[kt][r] * sc : -INFINITY;
-                sacc[kt][r] = v;
-                bm = fmaxf(bm, v);
+                for (int kt = 0; kt < kLKB / 16; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sacc[u][kt][r]);
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < kLKB / 16; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int rho = kt * 16 + 4 * fg + r;
+                        const float v = k0 + (kB ? lrow_key(rho) : rho) < n ? sacc[u][kt][r] : -INFINITY;
+                        sacc[u][kt][r] = v;
+                        bm = fmaxf(bm, v);
+                    }
             }
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bm);
-        const float alpha = exp2f(m - mn);          // 0 on the first block
-        float bs = 0.f;
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float bms = bm * sc;
+            if (__builtin_amdgcn_ballot_w64(bms > m[u] + kLazy) != 0) {
+                const float mn = fmaxf(m[u], bms);
+                const float alpha = m[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[u] - mn);
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = exp2f(sacc[kt][r] - mn);
-                sacc[kt][r] = p;
-                bs += p;
+                for (int dt = 0; dt <= kHd / 16; ++dt) o[u][dt] = o[u][dt] * alpha;
+                l[u] *= alpha;
+                m[u] = mn;
             }
-        bs += __shfl_xor(bs, 16);
-        bs += __shfl_xor(bs, 32);
-        l = l * alpha + bs;
-        m = mn;
+            const float mref = m[u] == -INFINITY ? 0.f : m[u];
+            float bs = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] = o[dt] * alpha;
-        if (sizeof(T) == 2) {
+            for (int kt = 0; kt < kLKB / 16; ++kt)
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                pv_step<VR>(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
+                for (int r = 0; r < 4; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][kt][r], sc, -mref));
+                    sacc[u][kt][r] = p;
+                    if constexpr (!kB) bs += p;
+                }
+            if constexpr (!kB) {
+                bs += __shfl_xor(bs, 16);
+                bs += __shfl_xor(bs, 32);
+                l[u] += bs;
+            }
+        }
+        if constexpr (kB) {
+#pragma unroll
+            for (int st = 0; st < kLKB / 32; ++st) {
+                lpv_step<QT, VR>(T(), vts, 32 * st, fr, fg, sacc, 2 * st, o);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
-                pv_step<VR>(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
+            for (int kt = 0; kt < kLKB / 16; ++kt) {
+                lpv_step<QT, VR>(T(), vts, 16 * kt, fr, fg, sacc, kt, o);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+    load_block(0, kvA, vvA);
+    if (kLKB < n) load_block(kLKB, kvB, vvB);
+    for (int k0 = 0; k0 < n; k0 += 2 * kLKB) {
+        process(k0, kvA, vvA);
+        if (k0 + kLKB < n) process(k0 + kLKB, kvB, vvB);
     }
-    const int q = qt * 16 + fr;
-    if (active && q < n) {
-        const float inv = 1.0f / l;
-        T* orow = out + (size_t)(s0 + q) * d + h * kHd;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            store4(orow + dt * 16 + 4 * fg, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    for (int u = 0; u < QT; ++u) {
+        const int q = qt0 * 16 + u * 16 + fr;
+        if (active && q < n) {
+            const float inv = 1.0f / (kB ? o[u][kHd / 16][0] : l[u]);
+            T* orow = out + (size_t)(s0 + q) * d + h * kHd;
+#pragma unroll
+            for (int dt = 0; dt < kHd / 16; ++dt)
+                store4(orow + dt * 16 + 4 * fg, o[u][dt][0] * inv, o[u][dt][1] * inv, o[u][dt][2] * inv,
+                       o[u][dt][3] * inv);
+        }
     }
 }
 
@@ -455,9 +593,13 @@ hipError_t attention(hipStream_t s, const T* qkv, const int* cu_seqlens, int n_w
     } else if (max_len <= kMaxWindow) {
         attention_kernel<T, kMaxWindow / 16><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);
     } else {
-        const int qgroups = (max_len + 63) / 64;
-        attention_long_kernel<T><<<n_windows * n_heads * qgroups, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d,
-                                                                             qgroups, out);
+        // bf16: 128 queries per workgroup, two 16-query tiles per wave; fp32: 64, one
+        constexpr int QT = sizeof(T) == 2 ? 2 : 1, QB = sizeof(T) == 2 ? 128 : 64;
+        const int qgroups = (max_len + QB - 1) / QB;
+        const int64_t blocks = (int64_t)n_windows * n_heads * qgroups;
+        if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+        attention_long_kernel<T, QT, QB><<<(unsigned)blocks, QB / QT * 4, 0, s>>>(qkv, cu_seqlens, n_heads, d,
+                                                                                  qgroups, out);
     }
     return hipGetLastError();
 }
