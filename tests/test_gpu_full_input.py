@@ -59,3 +59,24 @@ def test_b06_full_input(tmp_path):
     rep = compare(dims, w, clips, out, taps)
     print("b06 full-input", rep, flush=True)
     enc.free()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_input_sharp_softmax(dtype):
+    """q and k projections times 8 (exact in bf16): scores with a standard
+    deviation near 9 in log2 units, so later 64-key blocks often raise a
+    query's running maximum past the lazy-rescale margin and the long-segment
+    kernel rescales its partial output after the first block."""
+    dims = dataclasses.replace(synth.DIMS_TINY, window_chunks=0, dtype=dtype)
+    w = synth.make_weights(dims, 130)
+    for l in range(dims.n_layers):
+        for f in ("q_w", "k_w"):
+            w[f"layers.{l}.{f}"] = w[f"layers.{l}.{f}"] * np.float32(8.0)
+    enc = make_encoder(dims, w)
+    lens = [480000, 16000 * 10 + 8000]
+    clips = [synth.speech_like_clip(n, [95, i]) for i, n in enumerate(lens)]
+    print(f"case: tiny {dtype} full-input, q/k weights x8", lens, flush=True)
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(dims, w, clips, out, taps)
+    print("sharp full-input", dtype, rep, flush=True)
+    enc.free()
