@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     const int win = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
     const int s0 = cu[win], n = cu[win + 1] - s0;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
     const int fr = lane & 15, fg = lane >> 4;
     const int nt = (n + 15) >> 4;                  // 16-row tiles in this window
     const size_t ld = 3 * (size_t)d;
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(QB / QT * 4) __attribute__((amdgpu_waves_per_eu(2))
     const int seg = sh / n_heads, h = sh % n_heads;
     const int s0 = cu[seg], n = cu[seg + 1] - s0;
     if (qg * QB >= n) return;                        // whole workgroup idle (uniform)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
     const int fr = lane & 15, fg = lane >> 4;
     const size_t ld = 3 * (size_t)d;
     const T* kbase_p = qkv + (size_t)s0 * ld + d + h * kHd;
