@@ -611,6 +611,10 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     const size_t o_qkv = slot((size_t)n_tok * 3 * D * sizeof(T));
     const size_t o_att = slot((size_t)n_tok * D * sizeof(T));
     const size_t o_u = slot((size_t)n_tok * std::max(F, D) * sizeof(T));
+    // split-K partial sums of the residual GEMMs (small batches only: up to
+    // 8 splits of [n_tok][D] fp32)
+    const size_t part_elems = n_tok <= 4096 ? (size_t)8 * n_tok * D : 0;
+    const size_t o_part = slot(part_elems * 4);
     size_t o_tstem = 0, o_tl0 = 0;
     if (e->taps) {
         o_tstem = slot((size_t)n_tok * D * 4);
@@ -659,6 +663,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     T* u = reinterpret_cast<T*>(P(o_u));
     float* tstem = e->taps ? reinterpret_cast<float*>(P(o_tstem)) : nullptr;
     float* tl0 = e->taps ? reinterpret_cast<float*>(P(o_tl0)) : nullptr;
+    float* part = part_elems ? reinterpret_cast<float*>(P(o_part)) : nullptr;
     hipStream_t s = e->stream;
 
     // ---------------- launches
@@ -713,10 +718,12 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
         QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b), h));
         QA_LAUNCH("qkv", qa::gemm_bias<T>(s, h, n_tok, D, e->W<T>(lw.qkv_w), 3 * D, e->W<float>(lw.qkv_b), qkv, false));
         QA_LAUNCH("attention", qa::attention<T>(s, qkv, d_cu, n_win, d.n_heads, D, max_seg, att));
-        QA_LAUNCH("o_proj", qa::gemm_bias_resid<T>(s, att, n_tok, D, e->W<T>(lw.o_w), D, e->W<float>(lw.o_b), x));
+        QA_LAUNCH("o_proj", qa::gemm_bias_resid<T>(s, att, n_tok, D, e->W<T>(lw.o_w), D, e->W<float>(lw.o_b), x,
+                                                   part, part_elems));
         QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b), h));
         QA_LAUNCH("fc1", qa::gemm_bias<T>(s, h, n_tok, D, e->W<T>(lw.fc1_w), F, e->W<float>(lw.fc1_b), u, true));
-        QA_LAUNCH("fc2", qa::gemm_bias_resid<T>(s, u, n_tok, F, e->W<T>(lw.fc2_w), D, e->W<float>(lw.fc2_b), x));
+        QA_LAUNCH("fc2", qa::gemm_bias_resid<T>(s, u, n_tok, F, e->W<T>(lw.fc2_w), D, e->W<float>(lw.fc2_b), x,
+                                                part, part_elems));
         if (l == 0 && e->taps)
             QA_LAUNCH("tap_layer0", hipMemcpyAsync(tl0, x, (size_t)n_tok * D * 4, hipMemcpyDeviceToDevice, s));
     }

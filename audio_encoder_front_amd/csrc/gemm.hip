@@ -286,6 +286,25 @@ struct EpiF32Bias {        // out = acc + bias, fp32
     }
 };
 
+// One K split of a split-K GEMM: the fp32 partial sum of the split's K range,
+// part[blockIdx.y][m][n] = acc (no bias; resid_reduce adds the splits).
+struct EpiPartial {
+    using S = float;
+    static constexpr bool kStaged = true;
+    static constexpr int kDiv = 1;
+    float* part;
+    int M, N;
+    __device__ f32x4 init(int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ void frag(f32x4 v, float* o) const {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = v[r];
+    }
+    __device__ uint4 pre(int, int) const { return zero16(); }
+    __device__ void row(int m, int n, uint4 c, uint4) const {
+        if (m < M && n < N) store_chunk(part + ((size_t)blockIdx.y * M + m) * N + n, c, N - n);
+    }
+};
+
 // SwiGLU of the Thinker FFN (qwenasr.cpp ARCHITECTURE.md, "Qwen3 Thinker
 // decoder": silu(gate) * up).  The gate and up weights are interleaved in
 // blocks of 16 rows (gate rows f..f+15, then up rows f..f+15, ...), so MFMA
@@ -412,8 +431,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
         for (int q = 0; q < BI; ++q) dma16_buf(rw, wl.boff(wlane, q, kw), sb + q * 1024);
     };
 
-    const int nk = (K + KSTEP - 1) / KSTEP;
-    issue(0, 0);
+    // K range of this workgroup: all of K, or split blockIdx.y of gridDim.y
+    // (split-K; its partial sums go to EpiPartial)
+    const int nk_all = (K + KSTEP - 1) / KSTEP;
+    const int kper = (nk_all + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int kt0 = (int)blockIdx.y * kper;
+    const int nk = max(0, min(nk_all, kt0 + kper) - kt0);
+    issue(kt0, 0);
     const int fr = lane & 15, fg = lane >> 4;
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -433,13 +457,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sw[kb] = swz<BKB>(fr, kb * 4 + fg) * 16;
     constexpr int MPK = sizeof(T) == 2 ? 1 : 4;   // MFMAs per 64-byte K block
-    for (int kt = 0; kt < nk; ++kt) {
-        // Loads of the next stage (past the last stage they fetch zeros into
-        // the idle buffer), kept in this basic block so that the scheduling
-        // below can spread them between the MFMA groups.
-        issue(kt + 1, (kt + 1) & 1);
-        const char* a = smem + (kt & 1) * STAGE + (wm * TM * 16 + fr) * BKB;
-        const char* bp = smem + (kt & 1) * STAGE + BM * BKB + (wn * TN * 16 + fr) * BKB;
+    for (int i = 0; i < nk; ++i) {
+        // Loads of the next stage (past the last stage of K they fetch zeros
+        // into the idle buffer, past the last of a split they fetch the next
+        // split's first stage unused), kept in this basic block so that the
+        // scheduling below can spread them between the MFMA groups.
+        const int kt = kt0 + i;
+        issue(kt + 1, (i + 1) & 1);
+        const char* a = smem + (i & 1) * STAGE + (wm * TM * 16 + fr) * BKB;
+        const char* bp = smem + (i & 1) * STAGE + BM * BKB + (wn * TN * 16 + fr) * BKB;
         // Fragments: the TM activation fragments of a 64-byte K block stay in
         // registers while the TN weight fragments stream through a two-ahead
         // prefetch; the next K block's activation fragments are fetched during
@@ -551,9 +577,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int BKB, int SITE, class AL, class EP>
-static hipError_t launch(hipStream_t s, const AL& al, int M, const T* w, int N, int K, const EP& ep) {
+static hipError_t launch(hipStream_t s, const AL& al, int M, const T* w, int N, int K, const EP& ep,
+                         int splits = 1) {
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    gemm_kernel<T, BM, BN, WM, WN, BKB, SITE, AL, EP><<<tm * tn, WM * WN * 64, 0, s>>>(al, w, N, K, tm, tn, ep);
+    gemm_kernel<T, BM, BN, WM, WN, BKB, SITE, AL, EP><<<dim3(tm * tn, splits), WM * WN * 64, 0, s>>>(al, w, N, K, tm,
+                                                                                                   tn, ep);
     return hipGetLastError();
 }
 
@@ -601,10 +629,63 @@ hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N,
     return run<kProj1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N});
 }
 
+// x[m][n] += bias[n] + (part[0][m][n] + part[1][m][n] + ...), the splits
+// added in a fixed order (deterministic), 4 values per thread.
+__global__ __launch_bounds__(256) void resid_reduce_kernel(float* __restrict__ x, const float* __restrict__ part,
+                                                           int splits, int M, int N, const float* __restrict__ bias) {
+    const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;      // index of a 4-value group
+    const int64_t per_row = N / 4;
+    if (i4 >= (int64_t)M * per_row) return;
+    const int64_t m = i4 / per_row;
+    const int n = (int)(i4 - m * per_row) * 4;
+    const size_t o = (size_t)m * N + n, plane = (size_t)M * N;
+    float4 acc = *reinterpret_cast<const float4*>(part + o);
+    for (int sp = 1; sp < splits; ++sp) {
+        const float4 p = *reinterpret_cast<const float4*>(part + sp * plane + o);
+        acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    const float4 b = *reinterpret_cast<const float4*>(bias + n);
+    float4* px = reinterpret_cast<float4*>(x + o);
+    const float4 r = *px;
+    *px = make_float4(r.x + (b.x + acc.x), r.y + (b.y + acc.y), r.z + (b.z + acc.z), r.w + (b.w + acc.w));
+}
+
+// Split-K for the residual GEMMs of small batches: when the 128 x 128 tiling
+// leaves most of the CUs idle and K is long, the K range is cut into up to
+// 8 splits (each at least 4 stages), the partial sums go to `part` and
+// resid_reduce adds them into x.  Returns the number of splits (1: none).
+template <typename T>
+static int resid_splits(int M, int K, int N, size_t part_elems) {
+    constexpr int KSTEP = 128 / (int)sizeof(T);
+    const int nk = (K + KSTEP - 1) / KSTEP;
+    const long big = (long)((M + 255) / 256) * ((N + 255) / 256);
+    const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+    if (big >= 200 || tiles >= 128 || nk < 8 || N % 4) return 1;
+    int sp = (int)std::min<long>(8, 256 / tiles);
+    sp = std::min(sp, nk / 4);
+    if (sp < 2) return 1;
+    const int kper = (nk + sp - 1) / sp;
+    sp = (nk + kper - 1) / kper;                                     // every split has a stage
+    if ((size_t)sp * M * N > part_elems) return 1;
+    return sp;
+}
+
 template <typename T>
 hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, int N,
-                           const float* bias, float* x) {
+                           const float* bias, float* x, float* part, size_t part_elems) {
     DenseA<T> al{a, M, K, K};
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const int sp = part ? resid_splits<T>(M, K, N, part_elems) : 1;
+    if (sp > 1) {
+        if (K % Elem<T>::per16) return hipErrorInvalidValue;
+        const EpiPartial ep{part, M, N};
+        const hipError_t st = N == K ? launch<T, 128, 128, 2, 2, 128, kOProj>(s, al, M, w, N, K, ep, sp)
+                                     : launch<T, 128, 128, 2, 2, 128, kFC2>(s, al, M, w, N, K, ep, sp);
+        if (st != hipSuccess) return st;
+        const int64_t groups = (int64_t)M * (N / 4);
+        resid_reduce_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(x, part, sp, M, N, bias);
+        return hipGetLastError();
+    }
     EpiResid ep{x, bias, M, N};
     if (N == K) return run<kOProj>(s, al, M, w, N, K, ep);
     return run<kFC2>(s, al, M, w, N, K, ep);
@@ -648,7 +729,7 @@ hipError_t thinker_logits(hipStream_t s, const T* a, const int* rows, int n_rows
     template hipError_t gemm_bias<T>(hipStream_t, const T*, int, int, const T*, int, const float*, T*, \
                                      bool);                                                           \
     template hipError_t gemm_bias_resid<T>(hipStream_t, const T*, int, int, const T*, int,            \
-                                           const float*, float*);                                     \
+                                           const float*, float*, float*, size_t);                     \
     template hipError_t gemm_bias_f32<T>(hipStream_t, const T*, int, int, const T*, int, const float*, \
                                          float*);
 template hipError_t thinker_gemm<float>(hipStream_t, int, const float*, int, int, const float*, int, const float*,

@@ -86,9 +86,11 @@ hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K,
 template <typename T>
 hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N, const float* bias,
                      T* out, bool gelu);
+// x += A . W^T + bias.  part (part_elems floats, may be null): workspace for
+// split-K, used when the batch is too small to fill the GPU with tiles.
 template <typename T>
 hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, int N,
-                           const float* bias, float* x);
+                           const float* bias, float* x, float* part = nullptr, size_t part_elems = 0);
 template <typename T>
 hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, int N,
                          const float* bias, float* out);
