@@ -710,9 +710,11 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     const bool c1_blocked = std::is_same<T, qa::bf16>::value && e->conv1_frag != 0;   // MFMA conv1 layout
     QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1, n_chunks, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b), c2, false, c1_blocked));
     QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2, n_chunks, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b), c3, true, false));
-    QA_LAUNCH("conv_out", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), x, nullptr));
+    QA_LAUNCH("conv_out", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), x, nullptr,
+                                          part, part_elems));
     if (e->taps)
-        QA_LAUNCH("tap_stem", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), tl0, tstem));
+        QA_LAUNCH("tap_stem", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), tl0, tstem,
+                                              part, part_elems));
     for (int l = 0; l < d.n_layers; ++l) {
         const LayerW& lw = e->layers[l];
         QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b), h));

@@ -612,10 +612,64 @@ hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win,
     return time_major ? run<kConv3>(s, al, M, w, C, 9 * C, ep) : run<kConv2>(s, al, M, w, C, 9 * C, ep);
 }
 
+// Split-K for the residual GEMMs and conv_out of small batches: when the
+// 128 x 128 tiling leaves most of the CUs idle and K is long, the K range is
+// cut into up to 8 splits (each at least 4 stages), the partial sums go to
+// `part`, and a reduction kernel adds them in a fixed order and applies the
+// epilogue (resid_reduce: into the residual; pe_reduce: plus the position
+// table).  Returns the number of splits (1: none).
+template <typename T>
+static int resid_splits(int M, int K, int N, size_t part_elems) {
+    constexpr int KSTEP = 128 / (int)sizeof(T);
+    const int nk = (K + KSTEP - 1) / KSTEP;
+    const long big = (long)((M + 255) / 256) * ((N + 255) / 256);
+    const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+    if (big >= 200 || tiles >= 128 || nk < 8 || N % 4) return 1;
+    int sp = (int)std::min<long>(8, 256 / tiles);
+    sp = std::min(sp, nk / 4);
+    if (sp < 2) return 1;
+    const int kper = (nk + sp - 1) / sp;
+    sp = (nk + kper - 1) / kper;                                     // every split has a stage
+    if ((size_t)sp * M * N > part_elems) return 1;
+    return sp;
+}
+
+// x[m][n] = (part[0][m][n] + part[1][m][n] + ...) + pe[src[m] % 13][n], the
+// splits added in a fixed order; tap[m][n] = the sum without the PE.
+__global__ __launch_bounds__(256) void pe_reduce_kernel(float* __restrict__ x, float* __restrict__ tap,
+                                                        const float* __restrict__ part, int splits, int M, int N,
+                                                        const float* __restrict__ pe, const int* __restrict__ src) {
+    const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_row = N / 4;
+    if (i4 >= (int64_t)M * per_row) return;
+    const int64_t m = i4 / per_row;
+    const int n = (int)(i4 - m * per_row) * 4;
+    const size_t o = (size_t)m * N + n, plane = (size_t)M * N;
+    float4 acc = *reinterpret_cast<const float4*>(part + o);
+    for (int sp = 1; sp < splits; ++sp) {
+        const float4 p = *reinterpret_cast<const float4*>(part + sp * plane + o);
+        acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    const float4 p = *reinterpret_cast<const float4*>(pe + (size_t)(src[m] % kChunkTok) * N + n);
+    *reinterpret_cast<float4*>(x + o) = make_float4(acc.x + p.x, acc.y + p.y, acc.z + p.z, acc.w + p.w);
+    if (tap) *reinterpret_cast<float4*>(tap + o) = acc;
+}
+
 template <typename T>
 hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K, const T* w, int N,
-                    const float* pe, float* x, float* tap) {
+                    const float* pe, float* x, float* tap, float* part, size_t part_elems) {
     GatherA<T> al{a, src, n_tok, K};
+    if (n_tok <= 0 || N <= 0) return hipSuccess;
+    const int sp = part ? resid_splits<T>(n_tok, K, N, part_elems) : 1;
+    if (sp > 1) {   // split-K (see resid_splits), the PE added in the reduction
+        if (K % Elem<T>::per16) return hipErrorInvalidValue;
+        const hipError_t st =
+            launch<T, 128, 128, 2, 2, 128, kConvOut>(s, al, n_tok, w, N, K, EpiPartial{part, n_tok, N}, sp);
+        if (st != hipSuccess) return st;
+        const unsigned blocks = (unsigned)(((int64_t)n_tok * (N / 4) + 255) / 256);
+        pe_reduce_kernel<<<blocks, 256, 0, s>>>(x, tap, part, sp, n_tok, N, pe, src);
+        return hipGetLastError();
+    }
     EpiPE ep{x, tap, pe, src, n_tok, N};
     return run<kConvOut>(s, al, n_tok, w, N, K, ep);
 }
@@ -648,26 +702,6 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(float* __restrict__ x
     float4* px = reinterpret_cast<float4*>(x + o);
     const float4 r = *px;
     *px = make_float4(r.x + (b.x + acc.x), r.y + (b.y + acc.y), r.z + (b.z + acc.z), r.w + (b.w + acc.w));
-}
-
-// Split-K for the residual GEMMs of small batches: when the 128 x 128 tiling
-// leaves most of the CUs idle and K is long, the K range is cut into up to
-// 8 splits (each at least 4 stages), the partial sums go to `part` and
-// resid_reduce adds them into x.  Returns the number of splits (1: none).
-template <typename T>
-static int resid_splits(int M, int K, int N, size_t part_elems) {
-    constexpr int KSTEP = 128 / (int)sizeof(T);
-    const int nk = (K + KSTEP - 1) / KSTEP;
-    const long big = (long)((M + 255) / 256) * ((N + 255) / 256);
-    const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
-    if (big >= 200 || tiles >= 128 || nk < 8 || N % 4) return 1;
-    int sp = (int)std::min<long>(8, 256 / tiles);
-    sp = std::min(sp, nk / 4);
-    if (sp < 2) return 1;
-    const int kper = (nk + sp - 1) / sp;
-    sp = (nk + kper - 1) / kper;                                     // every split has a stage
-    if ((size_t)sp * M * N > part_elems) return 1;
-    return sp;
 }
 
 template <typename T>
@@ -725,7 +759,7 @@ hipError_t thinker_logits(hipStream_t s, const T* a, const int* rows, int n_rows
     template hipError_t conv3x3s2<T>(hipStream_t, const T*, int, int, int, int, const T*, const float*, \
                                      T*, bool, bool);                                                 \
     template hipError_t conv_out<T>(hipStream_t, const T*, const int*, int, int, const T*, int,        \
-                                    const float*, float*, float*);                                    \
+                                    const float*, float*, float*, float*, size_t);                                    \
     template hipError_t gemm_bias<T>(hipStream_t, const T*, int, int, const T*, int, const float*, T*, \
                                      bool);                                                           \
     template hipError_t gemm_bias_resid<T>(hipStream_t, const T*, int, int, const T*, int,            \

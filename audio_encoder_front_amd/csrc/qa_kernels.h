@@ -78,9 +78,11 @@ hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win,
                      const T* w, const float* bias, T* out, bool time_major, bool blocked_in);
 // x[t][:] = A[src[t]][:] . Wout^T + pe[src[t] % 13][:]  (fp32), and optionally
 // tap[t][:] without the PE.
+// part (part_elems floats, may be null): workspace for split-K, used when
+// the batch is too small to fill the GPU with tiles.
 template <typename T>
 hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K, const T* w, int N,
-                    const float* pe, float* x, float* tap);
+                    const float* pe, float* x, float* tap, float* part = nullptr, size_t part_elems = 0);
 
 // ---- dense GEMMs: out[M][N] = A[M][K] . W[N][K]^T + bias
 template <typename T>
