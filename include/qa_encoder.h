@@ -69,7 +69,7 @@ typedef struct qa_dims {
     int ffn_dim;          /* encoder_ffn_dim, multiple of 64 */
     int output_dim;       /* output_dim, multiple of 64 */
     int chunk_frames;     /* n_window * 2: must be 100 */
-    int window_chunks;    /* n_window_infer / chunk_frames: 1..8 (8 -> 104-token windows), or 0 for
+    int window_chunks;    /* n_window_infer / chunk_frames: 1..9 (8 -> 104-token windows, 9 -> 117), or 0 for
                              full-input attention: one segment per clip, clips of at most 30 s
                              (OneSpeech "Front end and graph numerics": the CPU graphs attend over
                              the whole bounded input; longer audio is chunked before encoding) */
