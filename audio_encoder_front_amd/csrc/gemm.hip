@@ -19,8 +19,9 @@
 // contiguously, i.e. 8 LDS rows of 128 B; lane l therefore fetches K-chunk
 // (l%8) ^ (row%8) of its row, an XOR swizzle that makes the 16-byte fragment
 // reads of 8 consecutive rows hit 8 different 16-byte bank groups.  Chunks
-// outside the matrix (ragged M/N/K, conv padding) read as zeros.  Two LDS
-// stages: loads of stage k+1 run while stage k is multiplied.
+// outside the matrix (ragged M/N/K, conv padding) read as zeros.  While
+// stage k is multiplied, the weights of stage k+1 and the A rows of stage
+// k+2 are in flight: a ring of three A stages and two weight stages.
 //
 // The MFMA is issued transposed (weights as the A operand): lane l then holds
 // 4 consecutive output columns of one output row.  After the K loop the tile
@@ -38,10 +39,11 @@ __device__ __align__(16) uint4 g_zero16[2];
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct-to-LDS loads written as inline asm: the compiler's wait-count pass
-// cannot tell the two LDS stages apart and would otherwise wait for the
-// in-flight stage k+1 loads before every LDS read of stage k.  Completion is
-// awaited explicitly (s_waitcnt vmcnt(0)) before the barrier that publishes
-// a stage.  M0 carries the wave's LDS destination; no other code in these
+// cannot tell the LDS stages apart and would otherwise wait for the
+// in-flight loads of later stages before every LDS read of stage k.
+// Completion is awaited explicitly (s_waitcnt vmcnt(n), leaving the n loads
+// of the stage two ahead in flight) before the barrier that publishes a
+// stage.  M0 carries the wave's LDS destination; no other code in these
 // kernels uses M0.
 //
 // Two forms.  buffer_load_dwordx4 ... lds reads through a buffer resource
@@ -214,7 +216,9 @@ __device__ __forceinline__ void store_chunk(S* p, uint4 c, int valid) {
     constexpr int E = Elem<S>::per16;
     if (valid >= E) { st16(p, c); return; }
     const S* e = reinterpret_cast<const S*>(&c);
-    for (int i = 0; i < valid; ++i) p[i] = e[i];
+#pragma unroll
+    for (int i = 0; i < E; ++i)                  // constant indices: c stays in registers
+        if (i < valid) p[i] = e[i];
 }
 
 template <typename T, bool kGelu>
@@ -378,10 +382,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     constexpr int KB = BKB / 64;              // 64-byte MFMA K blocks per stage
     constexpr int AI = BM / (RPD * NW);       // direct-to-LDS loads per wave per stage (A)
     constexpr int BI = BN / (RPD * NW);
-    constexpr int STAGE = (BM + BN) * BKB;    // bytes per LDS stage
+    constexpr int ASTAGE = BM * BKB;          // bytes per LDS stage of A
+    constexpr int BSTAGE = BN * BKB;          // of the weights
+    constexpr int STAGE = ASTAGE + BSTAGE;
     static_assert(BM % (RPD * NW) == 0 && BN % (RPD * NW) == 0, "tile/waves mismatch");
     static_assert(TN >= 3, "the two-ahead weight prefetch needs at least 3 weight tiles");
-    __shared__ __align__(1024) char smem[2 * STAGE];
+    // Three stages of A (a ring: its loads run two stages ahead), then two of
+    // the weights (one stage ahead): 160 KB for the 256 x 256 tile.
+    __shared__ __align__(1024) char smem[3 * ASTAGE + 2 * BSTAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
@@ -416,17 +424,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_void*)smem;
     const unsigned wave_u = (unsigned)__builtin_amdgcn_readfirstlane(wave);
     constexpr int KSTEP = BKB / (int)sizeof(T);   // K elements per stage
-    auto issue = [&](int kt, int buf) {
-        const int k0 = kt * KSTEP + kc * PER;
-        const auto kx = al.kprep(k0);
-        const auto kw = wl.kprep(k0);
-        const unsigned sa = lds0 + buf * STAGE + wave_u * (AI * 1024);
-        const unsigned sb = lds0 + buf * STAGE + BM * BKB + wave_u * (BI * 1024);
+    auto issue_a = [&](int kt, int buf) {
+        const auto kx = al.kprep(kt * KSTEP + kc * PER);
+        const unsigned sa = lds0 + buf * ASTAGE + wave_u * (AI * 1024);
 #pragma unroll
         for (int q = 0; q < AI; ++q) {
             if constexpr (AL::kBuffer) dma16_buf(ra, al.boff(alane, q, kx), sa + q * 1024);
             else dma16(al.addr(alane, q, kx), sa + q * 1024);
         }
+    };
+    auto issue_b = [&](int kt, int buf) {
+        const auto kw = wl.kprep(kt * KSTEP + kc * PER);
+        const unsigned sb = lds0 + 3 * ASTAGE + buf * BSTAGE + wave_u * (BI * 1024);
 #pragma unroll
         for (int q = 0; q < BI; ++q) dma16_buf(rw, wl.boff(wlane, q, kw), sb + q * 1024);
     };
@@ -437,7 +446,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     const int kper = (nk_all + (int)gridDim.y - 1) / (int)gridDim.y;
     const int kt0 = (int)blockIdx.y * kper;
     const int nk = max(0, min(nk_all, kt0 + kper) - kt0);
-    issue(kt0, 0);
+    issue_a(kt0, 0);
+    issue_b(kt0, 0);
+    issue_a(kt0 + 1, 1);
     const int fr = lane & 15, fg = lane >> 4;
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -462,10 +473,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
         // into the idle buffer, past the last of a split they fetch the next
         // split's first stage unused), kept in this basic block so that the
         // scheduling below can spread them between the MFMA groups.
+        // The A loads run two stages ahead (the activations and the conv
+        // input come from HBM more often than the L2-resident weights), issued
+        // after the weights' one-ahead loads so that the wait at the end of
+        // the iteration can leave them in flight: vector-memory loads complete
+        // in issue order.
         const int kt = kt0 + i;
-        issue(kt + 1, (i + 1) & 1);
-        const char* a = smem + (i & 1) * STAGE + (wm * TM * 16 + fr) * BKB;
-        const char* bp = smem + (i & 1) * STAGE + BM * BKB + (wn * TN * 16 + fr) * BKB;
+        const int abuf = i % 3;
+        issue_b(kt + 1, (i + 1) & 1);
+        issue_a(kt + 2, abuf == 0 ? 2 : abuf - 1);
+        const char* a = smem + abuf * ASTAGE + (wm * TM * 16 + fr) * BKB;
+        const char* bp = smem + 3 * ASTAGE + (i & 1) * BSTAGE + (wn * TN * 16 + fr) * BKB;
         // Fragments: the TM activation fragments of a 64-byte K block stay in
         // registers while the TN weight fragments stream through a two-ahead
         // prefetch; the next K block's activation fragments are fetched during
@@ -511,9 +529,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
                 __builtin_amdgcn_sched_group_barrier(0x008, TM * MPK, 0);
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // everything but this iteration's AI A loads: stage i + 1 has landed
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AI) : "memory");
         __syncthreads();
     }
+    // the last A loads (zeros or an unused stage) land before the epilogue
+    // reuses the LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     // acc[i][j] lane holds out[m = row fr][n = 4 fg + r] of tile (i, j)
     if constexpr (EP::kStaged) {
         // Staged epilogue: the lanes write their converted values row-major
