@@ -208,3 +208,24 @@ def test_bf16_wide_stem_valu_conv1():
     rep = compare(dims, w, clips, out, taps)
     _print("wide stem", rep)
     enc.free()
+
+
+@pytest.mark.parametrize("d_model,n_heads,ffn_dim", [(64, 1, 64), (128, 2, 192)])
+def test_bf16_short_k_gemms(d_model, n_heads, ffn_dim):
+    """bf16 encoders so narrow that the GEMMs run 1 to 3 K stages of 64
+    values (q/k/v, O-proj, FC1, FC2, proj1, proj2 with K = d or FFN): the
+    A-operand ring then fetches stages past the end of K (zeros) from its
+    first iteration on; conv_out (K = 32 x 16 = 512, 8 stages) splits K for
+    this small batch."""
+    import dataclasses
+    dims = dataclasses.replace(synth.DIMS_TINY, d_model=d_model, n_heads=n_heads, ffn_dim=ffn_dim,
+                               output_dim=d_model, dtype="bf16")
+    w = synth.make_weights(dims, 130 + d_model)
+    enc = make_encoder(dims, w)
+    lens = [16000 * 3 + 160 * 37 + 11, 16000]
+    clips = [synth.speech_like_clip(n, [95, i]) for i, n in enumerate(lens)]
+    _print(f"case: bf16 d={d_model} heads={n_heads} ffn={ffn_dim}", lens)
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(dims, w, clips, out, taps)
+    _print("short-K GEMMs", rep)
+    enc.free()
