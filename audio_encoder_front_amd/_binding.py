@@ -243,6 +243,11 @@ def qa_encoder_enable_taps(enc: Encoder, enable: bool) -> None:
 
 
 def qa_encoder_tap(enc: Encoder, tap: int, dst) -> int:
+    """Copy tap `tap` of the last encode into `dst`, a contiguous float32
+    device tensor (its element count is the capacity the library checks)."""
+    import torch
+    if dst is None or not dst.is_cuda or dst.dtype != torch.float32 or not dst.is_contiguous():
+        raise QAError(QA_STATUS_INVALID_PARAMS, "tap destination must be a contiguous float32 device tensor")
     n = _lib.qa_encoder_tap(enc.handle, tap, C.c_void_p(dst.data_ptr()), dst.numel())
     if n < 0:
         raise QAError(QA_STATUS_INVALID_PARAMS, qa_last_error())
@@ -275,7 +280,11 @@ def qa_encoder_free(enc: Encoder) -> None:
 def encode(enc: Encoder, pcm, lengths: Sequence[int], out=None):
     """Allocate `out` (torch, on pcm's device) if needed and run qa_encode."""
     import torch
-    total = sum(qa_encode_num_tokens(int(x)) for x in lengths)
+    counts = [qa_encode_num_tokens(int(x)) for x in lengths]
+    for i, c in enumerate(counts):
+        if c < 0:
+            raise QAError(QA_STATUS_INVALID_PARAMS, f"clip {i}: {qa_last_error()}")
+    total = sum(counts)
     if out is None:
         out = torch.empty((total, enc.dims.output_dim), dtype=torch.float32, device=pcm.device)
     qa_encode(enc, pcm, lengths, out)

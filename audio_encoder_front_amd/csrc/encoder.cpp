@@ -565,8 +565,12 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
         const int64_t len = lengths[i];
         const int nf = (int)(len / kHop);
         clips[i] = qa::ClipInfo{sample_off, (int32_t)len, (int32_t)frame_row};
-        for (int f0 = 0; f0 < nf; f0 += qa::kFrontFrames)
-            tiles.push_back(qa::FrontTile{i, f0, std::min(qa::kFrontFrames, nf - f0), 0});
+        // front-end tiles cover the nf kept frames and the final STFT frame:
+        // the front end computes that frame (not stored) so that every sample
+        // of the clip is read and checked, and its power too
+        const int nf_all = len > 0 ? nf + 1 : 0;
+        for (int f0 = 0; f0 < nf_all; f0 += qa::kFrontFrames)
+            tiles.push_back(qa::FrontTile{i, f0, std::min(qa::kFrontFrames, nf_all - f0), 0});
         const int tok0 = (int)tok_src.size();
         for (int c0 = 0; c0 < nf; c0 += qa::kChunk) {
             const int m = std::min(qa::kChunk, nf - c0);

@@ -62,6 +62,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const int L = c.len;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nsamp = 160 * (t.nframes - 1) + 400;
+    // frames past the clip's kept range (the final STFT frame, which the
+    // planner gives to the clip's last tile so that every sample is read and
+    // its power checked) are computed but neither stored nor in the maximum
+    const int nkeep = min(t.nframes, L / 160 - t.frame0);
     bool bad = false;
     // Samples in pairs (a pair never straddles a pad): every load of the tile
     // is issued before the first split, then each part plane gets one
@@ -178,6 +182,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             for (int r = 0; r < 4; ++r) {
                 const float re = acc[slot][0][ft][r], im = acc[slot][1][ft][r];
                 pwr[r] = re * re + im * im;
+                bad |= !isfinite(pwr[r]);              // power beyond float32 range
             }
             *reinterpret_cast<f32x4*>(pw + (16 * ft + li) * kPStride + 16 * bc + 4 * g) = pwr;
         }
@@ -197,7 +202,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         float e = 0.0f;
 #pragma unroll
         for (int j = 0; j < kMelTaps; ++j) e = fmaf(w[j], pr[j], e);
-        bad |= !isfinite(e);                     // power beyond float32 range
+        bad |= !isfinite(e);                     // mel energy beyond float32 range
+        if (f >= nkeep) continue;                // the dropped final frame
         const float lg = log10f(fmaxf(e, 1e-10f));
         outp[(size_t)f * kMels] = lg;
         vmax = fmaxf(vmax, lg);
@@ -215,8 +221,9 @@ __global__ __launch_bounds__(256) void normalize_kernel(float* __restrict__ logm
     const FrontTile t = tiles[blockIdx.x];
     const float mx = key_float(clip_key[t.clip]);
     const float lo = mx - 8.0f;
-    float4* p = reinterpret_cast<float4*>(logmel + (size_t)(clips[t.clip].frame_row0 + t.frame0) * kMels);
-    const int n4 = t.nframes * kMels / 4;
+    const ClipInfo c = clips[t.clip];
+    float4* p = reinterpret_cast<float4*>(logmel + (size_t)(c.frame_row0 + t.frame0) * kMels);
+    const int n4 = max(0, min(t.nframes, c.len / 160 - t.frame0)) * kMels / 4;   // kept frames only
     for (int i = threadIdx.x; i < n4; i += 256) {
         float4 v = p[i];
         v.x = (fmaxf(v.x, lo) + 4.0f) * 0.25f;

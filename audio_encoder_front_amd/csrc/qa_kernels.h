@@ -16,11 +16,14 @@ struct ClipInfo {
     int32_t frame_row0;
 };
 
-// A front-end tile: up to 64 consecutive frames of one clip.
+// A front-end tile: up to 64 consecutive STFT frames of one clip.  A clip of
+// L samples has floor(L/160) kept frames plus the final frame, which its last
+// tile computes (so every sample is read and its power checked) but does not
+// store.
 struct FrontTile {
     int32_t clip;
     int32_t frame0;      // first frame, counted within the clip
-    int32_t nframes;     // 1..64
+    int32_t nframes;     // 1..64, kept and final frames
     int32_t pad_;
 };
 

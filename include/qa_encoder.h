@@ -36,25 +36,29 @@ extern "C" {
 
 #define QA_ABI_VERSION 1
 
-/* Status codes (qwenasr.cpp "Public API" numbering). */
-#define QA_STATUS_OK              0
-#define QA_STATUS_INVALID_PARAMS (-1)
-#define QA_STATUS_LOAD_FAILED    (-2)
-#define QA_STATUS_ENCODE_FAILED  (-3)
-#define QA_STATUS_OOM            (-4)
+/* Status codes (qwenasr.cpp "Public API" numbering).  Functions returning
+ * int return one of these. */
+typedef enum qa_status {
+    QA_STATUS_OK = 0,
+    QA_STATUS_INVALID_PARAMS = -1,
+    QA_STATUS_LOAD_FAILED = -2,
+    QA_STATUS_ENCODE_FAILED = -3,
+    QA_STATUS_OOM = -4
+} qa_status;
 
 /* Element type of the weights handed to qa_encoder_create, and the operand
  * precision of every contraction.  QA_DTYPE_BF16: bf16 operands rounded to
  * nearest-even at operator boundaries, fp32 accumulation, fp32 residual
  * stream, LayerNorm statistics and softmax (OneSpeech "Front end and graph
  * numerics").  The DFT and mel contractions are fp32 in both modes. */
-#define QA_DTYPE_F32  0
-#define QA_DTYPE_BF16 1
+typedef enum qa_dtype { QA_DTYPE_F32 = 0, QA_DTYPE_BF16 = 1 } qa_dtype;
 
 /* Tap ids for qa_encoder_tap (stage outputs of the last qa_encode). */
-#define QA_TAP_LOG_MEL 0   /* normalised log-mel, fp32 [total_frames x 128], frame-major, clips in order */
-#define QA_TAP_STEM    1   /* conv_out output before PE, fp32 [total_tokens x d_model] */
-#define QA_TAP_LAYER0  2   /* residual stream after encoder layer 0, fp32 [total_tokens x d_model] */
+typedef enum qa_tap {
+    QA_TAP_LOG_MEL = 0,   /* normalised log-mel, fp32 [total_frames x 128], frame-major, clips in order */
+    QA_TAP_STEM = 1,      /* conv_out output before PE, fp32 [total_tokens x d_model] */
+    QA_TAP_LAYER0 = 2     /* residual stream after encoder layer 0, fp32 [total_tokens x d_model] */
+} qa_tap;
 
 /* Encoder dimensions; the field names follow the audio.* metadata keys of the
  * qwenasr.cpp "GGUF layout" section. */
@@ -73,7 +77,7 @@ typedef struct qa_dims {
                              full-input attention: one segment per clip, clips of at most 30 s
                              (OneSpeech "Front end and graph numerics": the CPU graphs attend over
                              the whole bounded input; longer audio is chunked before encoding) */
-    int dtype;            /* QA_DTYPE_F32 or QA_DTYPE_BF16 */
+    qa_dtype dtype;       /* QA_DTYPE_F32 or QA_DTYPE_BF16 (an int-sized enum) */
 } qa_dims;
 
 /* Weights: HOST pointers in PyTorch layouts, element type = dims.dtype
@@ -106,10 +110,18 @@ int qa_abi_version(void);
 const char *qa_last_error(void);
 
 /* Number of encoder tokens (output rows) of one clip of n_samples samples,
- * with 100-frame chunks: F = n_samples / 160 frames, 13 tokens per full chunk
- * and ceil(m / 8) for a tail of m frames.  0 for an empty clip; -1 (and
- * qa_last_error set) if 1 <= n_samples <= 200, n_samples < 0 or n_samples >
- * 19,200,000 (20 minutes).  Pure host arithmetic. */
+ * with 100-frame chunks: F = n_samples / 160 frames (OneSpeech "Front end and
+ * graph numerics": sample_count / 160 frames, the final STFT frame dropped),
+ * cut into chunks of 100 frames that each yield up to 13 tokens (same
+ * section); a chunk of m frames yields the stem's output length, m halved
+ * and rounded up three times (qwenasr.cpp "Conv2d subsampling stem": three
+ * stride-2 convolutions and the after-cnn length), i.e. 13 for a full chunk
+ * and ceil(m / 8) for a tail.  0 for an empty clip (OneSpeech "Low-level
+ * recognition": empty audio gives an empty result); -1 (and qa_last_error
+ * set) if 1 <= n_samples <= 200 (same section: nonempty audio must exceed
+ * 200 samples), n_samples < 0 or n_samples > 19,200,000 (M* ASR page,
+ * "Serving notes": a request holds at most 20 minutes).  Pure host
+ * arithmetic. */
 int64_t qa_encode_num_tokens(int64_t n_samples);
 
 /* Validate dims and weights, copy and repack the weights into device memory
@@ -122,12 +134,17 @@ qa_encoder *qa_encoder_create(const qa_weights *w, const qa_dims *d);
  * NULL = the null stream).  Returns QA_STATUS_OK or INVALID_PARAMS. */
 int qa_encoder_set_stream(qa_encoder *e, void *hip_stream);
 
-/* Encode a packed batch.
+/* Encode a packed batch: every step of the tower above, one packed forward
+ * over all clips with one attention segment per window of every clip (M* ASR
+ * page, Qwen3-ASR "Graph"; qwenasr.cpp "Windowed audio tower").
  *   pcm      DEVICE pointer, float32, all clips concatenated in `lengths`
  *            order (sum(lengths) samples, 16 kHz mono).  Caller-owned.
  *   lengths  HOST array of n_clips int64 sample counts.  0 = empty clip (no
  *            tokens); otherwise 201 .. 19,200,000 (201 .. 480,000 with
- *            full-input attention, dims.window_chunks = 0).
+ *            full-input attention, dims.window_chunks = 0): the bounds of
+ *            qa_encode_num_tokens (OneSpeech "Low-level recognition", M*
+ *            "Serving notes"; 30 s per OneSpeech "Front end and graph
+ *            numerics" for full-input attention).
  *   n_clips  >= 0.
  *   out      DEVICE pointer, float32 [sum_i qa_encode_num_tokens(lengths[i])
  *            x output_dim], rows clip-major, then chunk, then token-in-chunk.
@@ -135,9 +152,13 @@ int qa_encoder_set_stream(qa_encoder *e, void *hip_stream);
  * All argument checks happen before any device work.  The work is enqueued
  * on the handle's stream; the call then synchronises that stream to read a
  * device-side validation flag.  Returns QA_STATUS_OK; INVALID_PARAMS for bad
- * arguments, a nonfinite sample or a mel energy beyond float32 range (then
- * `out` is unspecified); OOM if the workspace cannot grow; ENCODE_FAILED on a
- * launch/runtime error.  Calls on one handle must not overlap. */
+ * arguments, a nonfinite sample (any sample of any clip) or a power or mel
+ * value beyond float32 range in any STFT frame, the dropped final frame
+ * included (OneSpeech "Low-level recognition": such inputs are rejected;
+ * then `out` is unspecified); OOM if the workspace cannot grow;
+ * ENCODE_FAILED on a launch/runtime error.  Mel energies are floored at
+ * 1e-10 and not capped above (OneSpeech "Front end and graph numerics").
+ * Calls on one handle must not overlap. */
 int qa_encode(qa_encoder *e, const float *pcm, const int64_t *lengths, int n_clips, float *out);
 
 /* Keep stage outputs of later qa_encode calls for qa_encoder_tap (costs one
@@ -193,7 +214,7 @@ typedef struct qa_thinker_dims {
     int head_dim;      /* attention.key_length: must be 128 */
     int ffn_dim;       /* feed_forward_length: multiple of 16 (3072 / 6144) */
     int vocab;         /* vocab_size (151936) */
-    int dtype;         /* QA_DTYPE_F32 or QA_DTYPE_BF16 */
+    qa_dtype dtype;    /* QA_DTYPE_F32 or QA_DTYPE_BF16 */
 } qa_thinker_dims;
 
 /* HOST pointers in PyTorch layouts (Linear = [out, in]), element type = dtype.

@@ -121,9 +121,17 @@ def log_mel_raw(x: np.ndarray) -> np.ndarray:
     F = floor(len/160) ([qwenasr] "Mel frontend": clamp then log; the trailing
     STFT frame is dropped; [OneSpeech] "power floor 1e-10").
 
+    Only the lower bound applies.  [qwenasr] "Mel frontend" also caps the mel
+    energy at 1e30 before the log; [OneSpeech] "Front end and graph numerics"
+    names only the 1e-10 floor and holds its features to the published float32
+    Whisper extractor, which has no cap, and "Low-level recognition" rejects
+    inputs whose power leaves the float32 range instead.  So energies in
+    (1e30, float32 max] keep their logarithm (above 30).
+
     Raises InvalidInput for a nonfinite sample or a power / mel value beyond
     float32 range ([OneSpeech] "Low-level recognition": such inputs are
-    rejected)."""
+    rejected).  The check covers every sample and every frame, including the
+    final STFT frame that is dropped from the output."""
     if not np.all(np.isfinite(x)):
         raise InvalidInput("nonfinite sample")
     fr = stft_frames(x)
@@ -320,7 +328,7 @@ def as_f64(W: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
 def encode_clip(x: np.ndarray, W: Dict[str, np.ndarray], n_layers: int, n_heads: int,
                 chunk: int = 100, window_chunks: int = 8,
                 windows: Optional[Sequence[int]] = None, tail: str = "A",
-                taps: Optional[dict] = None) -> Dict[int, np.ndarray]:
+                taps: Optional[dict] = None, mel: Optional[np.ndarray] = None) -> Dict[int, np.ndarray]:
     """Forward of one clip.  Returns {window index: output rows [w, out]}.
 
     window_chunks = 0 selects full-input attention: the whole clip (at most
@@ -331,13 +339,16 @@ def encode_clip(x: np.ndarray, W: Dict[str, np.ndarray], n_layers: int, n_heads:
     after it, chunks never mix and attention never crosses a window, so a
     window's rows depend only on its own 8 chunks.  `windows` selects which
     windows to compute (all if None) -- the definition restricted to them.
+    `mel` is this clip's log_mel(x) when the caller already has it (several
+    calls over disjoint windows of one clip then share it).
     """
     validate_clip(x.shape[0])
     if window_chunks == 0 and x.shape[0] > MAX_FULL_INPUT:
         raise InvalidInput("full-input attention takes clips of at most 30 s")
     if x.shape[0] == 0:
         return {}
-    mel = log_mel(x)
+    if mel is None:
+        mel = log_mel(x)
     if taps is not None:
         taps["log_mel"] = mel
     lens = chunk_lengths(mel.shape[1], chunk)

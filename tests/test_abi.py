@@ -127,3 +127,17 @@ def test_resample_length_matches_oracle(qa):
     assert qa.qa_resample_length(10, 999) == -1
     with pytest.raises(qa.QAError):
         qa.qa_resampler_create(768001)
+
+
+def test_binding_checks_lengths_and_tap_buffers_before_the_library(qa):
+    """encode() refuses an invalid clip length before it sizes `out`, and
+    qa_encoder_tap refuses a destination that is not a contiguous float32
+    device tensor (the library copies 4 bytes per counted element)."""
+    import torch
+    enc = qa._binding.Encoder(None, qa._binding.make_dims(synth.DIMS_TINY))
+    with pytest.raises(qa.QAError) as ei:
+        qa.encode(enc, torch.zeros(300), [300, 150])
+    assert ei.value.status == qa._binding.QA_STATUS_INVALID_PARAMS and "clip 1" in str(ei.value)
+    for dst in (torch.zeros(8), torch.zeros(8, dtype=torch.bfloat16)):
+        with pytest.raises(qa.QAError):
+            qa.qa_encoder_tap(enc, qa._binding.QA_TAP_LOG_MEL, dst)

@@ -7,7 +7,7 @@ import pytest
 
 import oracle as O
 import synth
-from parity_util import compare, make_encoder, run_gpu, workload_inputs
+from parity_util import compare, make_encoder, run_gpu, tail_reading_check, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,10 @@ def test_tiny_encoder_ragged_batch(tiny):
     assert out.shape[0] == sum(O.clip_num_tokens(n) for n in lens)
     rep = compare(wl.dims, w, clips, out, taps)
     _print("ragged", rep)
+    # tails of 1, 25 and 75 frames end in a row where the readings differ
+    rows = tail_reading_check(wl.dims, w, clips, taps)
+    _print("tail rows (clip, frames, vs A, vs B)", rows)
+    assert {m for _, m, _, _ in rows} >= {1, 25, 75}
 
 
 def test_tiny_encoder_silence_and_tone_edges(tiny):
@@ -81,6 +85,55 @@ def test_rejects_nonfinite_and_short_clips(tiny):
     x = synth.speech_like_clip(8000, [79, 1])
     res, _ = run_gpu(enc, [x])
     compare(wl.dims, w, [x], res, None)
+
+
+def test_rejects_trailing_nan_and_power_overflow_outside_the_bands(tiny):
+    """Every sample is checked, also those that only the dropped final STFT
+    frame reads (L mod 160 >= 41), and every power bin, also bin 0 which no
+    mel band weighs (OneSpeech "Low-level recognition": nonfinite samples and
+    power beyond float32 are rejected)."""
+    import torch
+    import audio_encoder_front_amd as qa
+    wl, _, w, enc = tiny
+    L = 160 * 50 + 150
+    out = torch.empty((qa.qa_encode_num_tokens(L), 256), device="cuda")
+    for case in ("nan at L-1", "nan at 160F+40", "dc 1e17"):
+        x = synth.speech_like_clip(L, [9, 4]).astype(np.float64)
+        if case == "nan at L-1":
+            x[L - 1] = np.nan
+        elif case == "nan at 160F+40":
+            x[160 * 50 + 40] = np.nan
+        else:
+            x = x + 1e17          # P_0 = 4e38 > float32 max; every mel band finite
+        _print("case:", case)
+        with pytest.raises(O.InvalidInput):
+            O.log_mel(x)
+        pcm = torch.from_numpy(x.astype(np.float32)).cuda()
+        with pytest.raises(qa.QAError) as ei:
+            qa.qa_encode(enc, pcm, [L], out)
+        assert ei.value.status == qa._binding.QA_STATUS_INVALID_PARAMS
+    # the sample just before the trailing range is read by a kept frame
+    x = synth.speech_like_clip(L, [9, 4])
+    x[160 * 50 + 39] = np.inf
+    pcm = torch.from_numpy(x).cuda()
+    with pytest.raises(qa.QAError):
+        qa.qa_encode(enc, pcm, [L], out)
+    # and a clean clip of that length still encodes
+    x = synth.speech_like_clip(L, [9, 5])
+    res, taps = run_gpu(enc, [x], taps=True)
+    compare(wl.dims, w, [x], res, taps)
+
+
+def test_loud_clip_keeps_mel_energies_above_1e30(tiny):
+    """Only the 1e-10 floor applies (no 1e30 cap): a clip scaled by 1e15 has
+    mel energies up to ~1e33, accepted and matching the oracle's log-mel."""
+    wl, _, w, enc = tiny
+    x = synth.speech_like_clip(16000 * 3 + 77, [9, 6]).astype(np.float64) * 1e15
+    assert O.log_mel_raw(x).max() > 30.5          # mel energies past 1e30
+    _print("case: loud clip x 1e15")
+    res, taps = run_gpu(enc, [x.astype(np.float32)], taps=True)
+    rep = compare(wl.dims, w, [x.astype(np.float32)], res, taps)
+    _print("loud", rep)
 
 
 def test_repeated_calls_shrink_and_grow_and_are_deterministic(tiny):
@@ -122,14 +175,14 @@ def test_b06_packed_32_clips(b06):
     clips = synth.make_audio(wl32)
     _print("case: 0.6B bf16, 32 clips U(1,30) s")
     out, taps = run_gpu(enc, clips, taps=True)
-    lens = [len(c) for c in clips]
-    order = np.argsort(lens)
-    picked = {int(order[0]), int(order[-1]), 7}
-    # every window of three clips (shortest, longest, one fixed), the last
-    # (ragged) window of all others; the log-mel of every clip
-    rep = compare(wl.dims, w, clips, out, taps,
-                  windows_per_clip=lambda ci, nw: range(nw) if ci in picked else [nw - 1])
+    # every window of every clip (73), per window and per row, and the
+    # log-mel of every clip
+    rep = compare(wl.dims, w, clips, out, taps, progress="b06_32")
+    assert rep["windows_checked"] == 73
     _print("b06_32", rep)
+    rows = tail_reading_check(wl.dims, w, clips, taps)
+    _print("b06_32 tail rows", len(rows))
+    assert len(rows) >= 8
 
 
 def test_b06_window_boundaries_and_tails(b06):
@@ -141,6 +194,8 @@ def test_b06_window_boundaries_and_tails(b06):
     out, taps = run_gpu(enc, clips, taps=True)
     assert out.shape[0] == 104 + 105 + 117 + 1
     compare(wl.dims, w, clips, out, taps)
+    rows = tail_reading_check(wl.dims, w, clips, taps)
+    assert {m for _, m, _, _ in rows} == {1}
 
 
 @pytest.fixture(scope="module")
@@ -152,27 +207,30 @@ def b17():
     enc.free()
 
 
-def test_b17_twenty_minutes_sampled_windows(b17):
+def test_b17_twenty_minutes_every_window(b17):
     wl, w, enc = b17
     clips = synth.make_audio(wl)
-    _print("case: 1.7B bf16, one 20-minute clip (sampled windows)")
+    _print("case: 1.7B bf16, one 20-minute clip (every window)")
     out, taps = run_gpu(enc, clips, taps=True)
     assert out.shape == (15600, 2048)
     assert np.all(np.isfinite(out))
-    rep = compare(wl.dims, w, clips, out, taps, windows_per_clip=lambda ci, nw: [0, 1, 73, nw - 2, nw - 1])
+    rep = compare(wl.dims, w, clips, out, taps, progress="b17_20m")
+    assert rep["windows_checked"] == 150
     _print("b17_20m", rep)
 
 
-def test_b17_packed_16_clips_sampled_windows(b17):
+def test_b17_packed_16_clips_every_window(b17):
     wl, w, enc = b17
     clips = synth.make_audio(synth.WORKLOADS["b17_16"])
-    _print("case: 1.7B bf16, 16 clips logU(10,300) s (sampled windows)")
+    _print("case: 1.7B bf16, 16 clips logU(10,300) s (every window)")
     out, taps = run_gpu(enc, clips, taps=True)
     assert out.shape == (21162, 2048)
-    shortest = int(np.argmin([len(c) for c in clips]))
-    rep = compare(wl.dims, w, clips, out, taps,
-                  windows_per_clip=lambda ci, nw: range(nw) if ci == shortest else [0, nw - 1])
+    rep = compare(wl.dims, w, clips, out, taps, progress="b17_16")
+    assert rep["windows_checked"] == 213
     _print("b17_16", rep)
+    rows = tail_reading_check(wl.dims, w, clips, taps)
+    _print("b17_16 tail rows", rows)
+    assert len(rows) >= 8
 
 
 @pytest.mark.parametrize("base,window_chunks", [("tiny", 9), ("tiny", 1), ("b06", 9)])

@@ -1,23 +1,31 @@
 """GPU parity of the audio splice + Thinker prefill against the oracle, through
 the C ABI: a fp32 miniature (every prompt of a ragged packed batch, several
-key blocks, spans at the prompt edges, a one-token prompt) and the 0.6B- and
-1.7B-shaped bf16 Thinkers (28 layers, 16/8 heads of 128, vocab 151936).
+key blocks, spans at the prompt edges, a one-token prompt), the 0.6B- and
+1.7B-shaped bf16 Thinkers (28 layers, 16/8 heads of 128, vocab 151936) and
+the 1.7B width at 6,251 packed tokens (every GEMM site on 256 x 256 tiles).
 
 The audio states are seeded stand-ins (oracle inputs never come from the GPU
 path).  Gated, per prompt, relative L2 of the final hidden states and of the
 last-token logits:
 * fp32: against the oracle, 1e-4 (as for the encoder);
-* bf16: against the oracle, hidden <= 3e-2 and logits <= 5e-2, and at most
-  twice (plus 1e-3) the distance from the oracle of the bf16 error model
-  (tests/thinker_bf16_model.py: the oracle with every value the GPU stores as
-  bf16 rounded at the same boundaries).  The model puts the policy's own
-  effect at 5.3e-3 / 9.7e-3 (hidden / logits) for the 0.6B shape and
-  1.4e-2 / 2.5e-2 for the 1.7B shape (28 layers of 8-bit operands with
-  N(0, 0.02) weights); the GPU lands at the same distance.  The rounding
-  decisions themselves are chaotic over 28 layers (the GPU and the model
-  round differently wherever fp32 accumulation order moves a value across a
-  bf16 boundary), so GPU and model differ from each other by about as much
-  as each differs from the oracle; that distance is reported, not gated."""
+* bf16: against the bf16 error model (tests/thinker_bf16_model.py: the oracle
+  with every value the GPU stores as bf16 rounded at the same boundaries,
+  everything else exact).  Model and GPU are two realisations of the same
+  rounding policy; each one's distance from the exact oracle is the norm of
+  an accumulation of very many rounding errors, and such norms concentrate:
+  over every bf16 case here the GPU's distance is 0.97 to 1.06 times the
+  model's for the hidden states and 0.76 to 1.08 times for the logits (one
+  row, fewer error sources, 28 layers of chaotic amplification at most).  A
+  kernel defect adds an error d roughly orthogonal to the rounding noise s,
+  so the GPU's distance becomes sqrt(s^2 + d^2); the gates
+      GPU vs oracle <= 1.15 x model vs oracle (hidden), 1.25 x (logits)
+  leave room for that spread and reject any d above 0.57 s (hidden) and
+  0.75 s (logits), i.e. a kernel error well below the policy's own effect.
+  A second check bounds GPU vs model by 1.6 x the model's distance (two
+  independent realisations differ by sqrt(2) s; measured 0.15 to 1.14 s).
+  Absolute ceilings of 3e-2 / 5e-2 keep the policy's effect itself in view;
+  the sharp-softmax case, whose policy effect alone is 3.1e-2, is held to
+  the relative gates only."""
 import numpy as np
 import pytest
 
@@ -28,6 +36,8 @@ import thinker_bf16_model as BM
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": (1e-4, 1e-4), "bf16": (3e-2, 5e-2)}     # (hidden, logits) against the oracle
+REL = (1.15, 1.25)          # bf16: GPU vs oracle over model vs oracle (hidden, logits)
+PAIR = 1.6                  # bf16: GPU vs model over model vs oracle
 
 
 def rel_l2(a, b):
@@ -57,13 +67,16 @@ def _check(dims, W, prompts, audio, hid, lg, tol=None):
         gh, gg = hid[row:row + len(ids)], lg[i]
         eh, eg = rel_l2(gh, rh), rel_l2(gg, rg)
         msg = f"  prompt {i}: {len(ids)} tokens, vs oracle hidden {eh:.3g} logits {eg:.3g}"
-        assert eh <= tol_h and eg <= tol_g, (i, eh, eg)
+        if tol_h is not None:
+            assert eh <= tol_h and eg <= tol_g, (i, eh, eg)
         if dims.dtype == "bf16":
             mh, mg = BM.prefill_prompt(*args)
             dh, dg = rel_l2(mh, rh), rel_l2(mg, rg)             # the policy's own effect
             ph, pg = rel_l2(gh, mh), rel_l2(gg, mg)             # GPU vs the policy model
-            msg += f"; model vs oracle {dh:.3g} / {dg:.3g}; GPU vs model {ph:.3g} / {pg:.3g}"
-            assert eh <= 2 * dh + 1e-3 and eg <= 2 * dg + 1e-3, (i, eh, eg, dh, dg)
+            msg += (f"; model vs oracle {dh:.3g} / {dg:.3g} (ratio {eh / dh:.3f} / {eg / dg:.3f}); "
+                    f"GPU vs model {ph:.3g} / {pg:.3g}")
+            assert eh <= REL[0] * dh + 1e-5 and eg <= REL[1] * dg + 1e-5, (i, eh, eg, dh, dg)
+            assert ph <= PAIR * dh + 1e-5 and pg <= PAIR * dg + 1e-5, (i, ph, pg, dh, dg)
         print(msg, flush=True)
         worst = (max(worst[0], eh), max(worst[1], eg))
         row += len(ids)
@@ -158,9 +171,9 @@ def test_bf16_thinker_long_prompts(hq, hkv, qk_gain):
     the lazy-rescale margin (8 in log2 units) and the rescale branch runs
     after the first block too.  A softmax this sharp amplifies the bf16
     rounding of q and k: the bf16 error model itself lands 3.1e-2 / 3.2e-2
-    (hidden / logits) from the oracle on the 18-token prompt, so that case
-    takes an absolute gate of about twice the model's distance (6e-2 / 8e-2);
-    the gate relative to the model's own distance is the same as elsewhere."""
+    (hidden / logits) from the oracle on the 18-token prompt, above the
+    absolute ceiling, so that case is held to the gates relative to the
+    model's own distance only (the same as elsewhere)."""
     d = ST.ThinkerDims(hidden=256, n_layers=2, n_q_heads=hq, n_kv_heads=hkv, ffn_dim=512, vocab=1000,
                        dtype="bf16")
     W = ST.make_weights(d, 240 + hq)
@@ -173,5 +186,33 @@ def test_bf16_thinker_long_prompts(hq, hkv, qk_gain):
     print(f"case: bf16 thinker long prompts, heads {hq}/{hkv}, qk gain {qk_gain}",
           [len(p[0]) for p in prompts], flush=True)
     hid, lg = _run(d, W, prompts, audio)
-    tol = (6e-2, 8e-2) if qk_gain > 1 else None
+    tol = (None, None) if qk_gain > 1 else None
     print("bf16 long-prompt thinker worst (hidden, logits)", _check(d, W, prompts, audio, hid, lg, tol), flush=True)
+
+
+def _big_tiles(m, n):
+    return ((m + 255) // 256) * ((n + 255) // 256)
+
+
+def test_bf16_thinker_1p7b_width_bench_tile_path():
+    """bf16 at the 1.7B width (hidden 2048, 16/8 heads of 128, FFN 6144), two
+    layers, three prompts packing 6,251 tokens.  With more than 6,144 rows
+    every GEMM site has at least 200 tiles of 256 x 256 (q/k/v 4096 wide: 400,
+    O-proj and down 2048 wide: 200, gate/up 12288 wide: 1200), so all of them
+    take the 256 x 256 path that the 15,617-token prefill runs, including the
+    paired SwiGLU epilogue; the longest prompt's last query block attends over
+    48 key blocks of 64.  A small vocabulary keeps the oracle cheap (the
+    logits GEMM has one row per prompt either way)."""
+    d = ST.ThinkerDims(hidden=2048, n_layers=2, n_q_heads=16, n_kv_heads=8, ffn_dim=6144, vocab=4096,
+                       dtype="bf16")
+    W = ST.make_weights(d, 270)
+    prompts = _prompts([3000, 2700, 500], d.vocab, 271)
+    M = sum(len(p[0]) for p in prompts)
+    assert M == 6251
+    for n in (d.hidden + 2 * d.n_kv_heads * d.head_dim, d.hidden, 2 * d.ffn_dim):
+        assert _big_tiles(M, n) >= 200
+    n_audio = sum(p[2] for p in prompts)
+    audio = ST.make_audio_states(n_audio, d.hidden, [272, 0])
+    print("case: bf16 thinker 1.7B width, 2 layers, prompts", [len(p[0]) for p in prompts], flush=True)
+    hid, lg = _run(d, W, prompts, audio)
+    print("bf16 1.7B-width thinker worst (hidden, logits)", _check(d, W, prompts, audio, hid, lg), flush=True)

@@ -165,3 +165,86 @@ def test_rejects_nonfinite_and_float32_overflow():
         O.log_mel(x)
     x[1234] = 1e3                       # large but representable
     assert np.all(np.isfinite(O.log_mel(x)))
+
+
+def test_tone_mel_closed_form_values():
+    # The noise-free 0.3 sin(2 pi 440 t) puts P_11 = 900 on interior frames and
+    # P_10 = P_12 = 225 (test above).  Band 18's triangle spans 420.89 ..
+    # 467.65 Hz (below 1 kHz the Slaney scale is 3 f / 200, so its edges are
+    # 18, 19, 20 steps of mel(8000)/129 mapped back linearly), so it holds
+    # bin 11 (440 Hz) only: fb[18, 11] = 0.8174 * 2 / 46.77 Hz = 0.0349524 and
+    # E_18 = 900 * 0.0349524 = 31.457.
+    fb = O.mel_filterbank()
+    assert fb[18, 11] == pytest.approx(0.0349524, abs=5e-8)
+    assert fb[18, 10] == 0.0 and fb[18, 12] == 0.0
+    t = np.arange(32000) / 16000.0
+    x = 0.3 * np.sin(2 * np.pi * 440.0 * t)
+    e = O.power_spectrum(O.stft_frames(x)) @ fb.T
+    assert np.allclose(e[2:198, 18], 31.457, atol=5e-4)
+
+
+def test_matches_published_whisper_feature_extractor():
+    """OneSpeech "Front end and graph numerics": the features agree with the
+    published float32 Whisper feature extractor to a max-abs 3e-5.  That
+    extractor (transformers' WhisperFeatureExtractor, 128 bins, no padding to
+    30 s) is an implementation independent of the oracle; its float32 path
+    must land within the page's 3e-5 and its float64 path within float32
+    rounding of the oracle."""
+    tr = pytest.importorskip("transformers")
+    fe = tr.WhisperFeatureExtractor(feature_size=128)
+    x = synth.make_audio(synth.WORKLOADS["b06_1"])[0][:16000 * 7 + 123]
+    ref = O.log_mel(x.astype(np.float64))
+    f32 = fe(x, sampling_rate=16000, padding="longest", return_tensors="np")["input_features"][0]
+    assert f32.shape == ref.shape
+    assert np.abs(f32 - ref).max() <= 3e-5
+    f64 = fe._np_extract_fbank_features(x.astype(np.float64)[None], "cpu")[0]
+    assert np.abs(f64 - ref).max() <= 2e-6
+    # the tiny workload (tone + noise), a 201-sample clip and a tail frame count
+    for clip in (synth.make_audio(synth.WORKLOADS["tiny"])[0], synth.speech_like_clip(201, [9, 1]),
+                 synth.speech_like_clip(16000 * 2 + 160 * 37 + 99, [9, 2])):
+        r = O.log_mel(clip.astype(np.float64))
+        f = fe._np_extract_fbank_features(clip.astype(np.float64)[None], "cpu")[0]
+        assert f.shape == r.shape and np.abs(f - r).max() <= 2e-6
+
+
+def test_no_upper_clamp_on_mel_energy():
+    """Reading of the pages' clamp: only the 1e-10 floor.  Scaling a clip by s
+    scales every power and mel energy by s^2, so the raw log-mel shifts by
+    exactly 2 log10(s) wherever the floor is inactive; at s = 1e15 the mel
+    energies reach ~1e31, past the 1e30 cap of qwenasr "Mel frontend", and
+    the shift still holds (a cap would pin them at 30).  The published
+    extractor agrees at that scale."""
+    x = synth.make_audio(synth.WORKLOADS["b06_1"])[0][:16000 * 3 + 77].astype(np.float64)
+    raw = O.log_mel_raw(x)
+    assert raw.min() > -10.0                         # the floor is not reached
+    big = O.log_mel_raw(x * 1e15)
+    assert big.max() > 31.0
+    assert np.abs(big - (raw + 30.0)).max() < 1e-9
+    tr = pytest.importorskip("transformers")
+    fe = tr.WhisperFeatureExtractor(feature_size=128)
+    f = fe._np_extract_fbank_features((x * 1e15)[None], "cpu")[0]
+    assert np.abs(f - O.log_mel(x * 1e15)).max() <= 2e-6
+
+
+def test_rejects_power_overflow_in_a_bin_outside_every_band():
+    # DC of 1e17: X_0 = 200e17 gives P_0 = 4e38 > float32 max, while the bins
+    # a mel band weighs stay finite (P_1 = 1e38): bin 0 lies outside every
+    # Slaney band, so the rejection must come from the power check itself.
+    x = np.full(5000, 1e17) + synth.speech_like_clip(5000, [9, 3]).astype(np.float64)
+    fr = O.stft_frames(x)
+    p = O.power_spectrum(fr)
+    assert p[:, 0].max() > O.F32_MAX
+    assert (p @ O.mel_filterbank().T).max() < O.F32_MAX
+    assert np.all(O.mel_filterbank()[:, 0] == 0.0)
+    with pytest.raises(O.InvalidInput):
+        O.log_mel(x)
+
+
+def test_rejects_nonfinite_trailing_sample():
+    # L = 160 F + r with r >= 41: samples 160 F + 40 .. L - 1 are read only by
+    # the final (dropped) STFT frame; they are still part of the input
+    L = 160 * 50 + 150
+    x = synth.speech_like_clip(L, [9, 4]).astype(np.float64)
+    x[L - 1] = np.nan
+    with pytest.raises(O.InvalidInput):
+        O.log_mel(x)
