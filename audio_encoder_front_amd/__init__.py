@@ -6,6 +6,7 @@ built.
 """
 from ._binding import *  # noqa: F401,F403
 from ._binding import (Encoder, QAError, encode, library, make_dims, qa_abi_version, qa_encode,  # noqa: F401
+                       qa_encode_noalloc,
                        qa_encode_num_tokens, qa_encoder_create, qa_encoder_enable_taps, qa_encoder_free,
                        qa_encoder_kernel_times, qa_encoder_set_profiling, qa_encoder_set_profiling_label,
                        qa_encoder_set_stream,

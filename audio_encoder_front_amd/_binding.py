@@ -25,9 +25,10 @@ QA_DTYPE_BF16 = 1
 QA_TAP_LOG_MEL = 0
 QA_TAP_STEM = 1
 QA_TAP_LAYER0 = 2
+QA_NOALLOC_SCRATCH_BYTES = 160 * 1024 * 1024
 
 EXPORTS = ("qa_abi_version", "qa_last_error", "qa_encode_num_tokens", "qa_encoder_create",
-           "qa_encoder_set_stream", "qa_encode", "qa_encoder_enable_taps", "qa_encoder_tap",
+           "qa_encoder_set_stream", "qa_encode", "qa_encode_noalloc", "qa_encoder_enable_taps", "qa_encoder_tap",
            "qa_encoder_set_profiling", "qa_encoder_kernel_times", "qa_encoder_set_profiling_label",
            "qa_encoder_free", "qa_resample_length", "qa_resampler_create", "qa_resample", "qa_resampler_free",
            "qa_thinker_create", "qa_thinker_set_stream", "qa_thinker_prefill", "qa_thinker_free")
@@ -88,6 +89,8 @@ def _load() -> C.CDLL:
     lib.qa_encoder_set_stream.argtypes = [C.c_void_p, C.c_void_p]
     lib.qa_encode.restype = C.c_int
     lib.qa_encode.argtypes = [C.c_void_p, C.c_void_p, C.POINTER(C.c_int64), C.c_int, C.c_void_p]
+    lib.qa_encode_noalloc.restype = C.c_int
+    lib.qa_encode_noalloc.argtypes = [C.c_void_p, C.c_void_p, C.POINTER(C.c_int64), C.c_int, C.c_void_p]
     lib.qa_encoder_enable_taps.restype = C.c_int
     lib.qa_encoder_enable_taps.argtypes = [C.c_void_p, C.c_int]
     lib.qa_encoder_tap.restype = C.c_int64
@@ -217,6 +220,17 @@ def qa_encoder_set_stream(enc: Encoder, stream) -> None:
 def qa_encode(enc: Encoder, pcm, lengths: Sequence[int], out) -> None:
     """pcm: device float32 tensor (all clips concatenated); lengths: host
     sequence of int; out: device float32 tensor [total_tokens, output_dim]."""
+    _encode_call(_lib.qa_encode, enc, pcm, lengths, out)
+
+
+def qa_encode_noalloc(enc: Encoder, pcm, lengths: Sequence[int], out) -> None:
+    """qa_encode on the library's fixed per-GPU scratch array (no allocation;
+    batches up to QA_NOALLOC_SCRATCH_BYTES of workspace; calls on one GPU
+    must not overlap)."""
+    _encode_call(_lib.qa_encode_noalloc, enc, pcm, lengths, out)
+
+
+def _encode_call(fn, enc: Encoder, pcm, lengths: Sequence[int], out) -> None:
     n = len(lengths)
     total = sum(int(x) for x in lengths)
     rows = 0
@@ -235,7 +249,7 @@ def qa_encode(enc: Encoder, pcm, lengths: Sequence[int], out) -> None:
     arr = (C.c_int64 * max(n, 1))(*[int(x) for x in lengths])
     pp = C.c_void_p(pcm.data_ptr() if pcm is not None and pcm.numel() else 0)
     op = C.c_void_p(out.data_ptr() if out is not None and out.numel() else 0)
-    _check(_lib.qa_encode(enc.handle, pp, arr, n, op))
+    _check(fn(enc.handle, pp, arr, n, op))
 
 
 def qa_encoder_enable_taps(enc: Encoder, enable: bool) -> None:

@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <type_traits>
@@ -68,6 +69,35 @@ int64_t tokens_of(int64_t n) {
 }
 
 bool valid_len(int64_t n) { return n == 0 || (n > 200 && n <= kMaxSamples); }
+
+// Workspace of qa_encode_noalloc: one fixed device array per GPU, held until
+// the process ends.  In host code `scratch` is only a handle; its device
+// address (different on every GPU) comes from hipGetSymbolAddress, taken once
+// per device when an encoder is created there, and only that address is
+// passed to kernels and copies.
+constexpr size_t kScratchBytes = QA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+bool g_scratch_tried[kMaxDevices] = {};
+
+// With `device` current: the device address of its scratch array (taken on
+// the first call for the device), or null with the error recorded.
+void* scratch_address(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_tried[device]) {
+        void* ptr = nullptr;
+        const hipError_t st = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_tried[device] = true;
+        g_scratch_err[device] = st;
+        g_scratch_ptr[device] = st == hipSuccess ? ptr : nullptr;
+        if (st != hipSuccess) (void)hipGetLastError();
+    }
+    return g_scratch_ptr[device];
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -459,6 +489,7 @@ QA_API qa_encoder* qa_encoder_create(const qa_weights* w, const qa_dims* d) {
     e->pe = put_f32(make_pe(D));
 
     hipError_t st = hipGetDevice(&e->device);
+    if (st == hipSuccess) (void)scratch_address(e->device);   // failure is reported by qa_encode_noalloc
     if (st == hipSuccess) st = hipMalloc(&e->wbuf, pk.host.size());
     if (st == hipSuccess) st = hipMemcpy(e->wbuf, pk.host.data(), pk.host.size(), hipMemcpyHostToDevice);
     if (st == hipSuccess) st = hipHostMalloc(&e->flag_host, sizeof(int), hipHostMallocDefault);
@@ -548,9 +579,21 @@ QA_API void qa_encoder_free(qa_encoder* e) {
 
 namespace {
 
+// A caller-fixed workspace (qa_encode_noalloc): nothing is allocated, the
+// tables go up from pageable host memory, and neither taps nor profiling
+// events are recorded.
+struct FixedWorkspace {
+    char* base;
+    size_t bytes;
+};
+
 template <typename T>
-int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_clips, float* out) {
+int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_clips, float* out,
+               const FixedWorkspace* fixed = nullptr) {
     const qa_dims& d = e->d;
+    const bool taps = e->taps && !fixed;
+    const bool profiling = e->profiling && !fixed;
+    if (fixed) e->tap_tokens = -1;      // the taps of an earlier call pointed into the growable workspace
     const int C = d.conv_channels, D = d.d_model, F = d.ffn_dim, O = d.output_dim;
     // ---------------- plan
     std::vector<qa::ClipInfo> clips(n_clips);
@@ -590,7 +633,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     if (n_tok > 0 && !out) { set_err("out is NULL but the batch has %d tokens", n_tok); return QA_STATUS_INVALID_PARAMS; }
     if (sample_off > 0 && !pcm) { set_err("pcm is NULL"); return QA_STATUS_INVALID_PARAMS; }
     if (n_tok == 0) {
-        if (e->taps) { e->tap_frames = 0; e->tap_tokens = 0; }
+        if (taps) { e->tap_frames = 0; e->tap_tokens = 0; }
         return QA_STATUS_OK;
     }
 
@@ -620,12 +663,18 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     const size_t part_elems = n_tok <= 4096 ? (size_t)8 * n_tok * D : 0;
     const size_t o_part = slot(part_elems * 4);
     size_t o_tstem = 0, o_tl0 = 0;
-    if (e->taps) {
+    if (taps) {
         o_tstem = slot((size_t)n_tok * D * 4);
         o_tl0 = slot((size_t)n_tok * D * 4);
     }
     const size_t need = off;
-    if (need > e->ws_size) {
+    if (fixed) {
+        if (need > fixed->bytes) {
+            set_err("this batch needs %zu bytes of workspace; qa_encode_noalloc holds at most %zu "
+                    "(use qa_encode, or a smaller batch)", need, fixed->bytes);
+            return QA_STATUS_INVALID_PARAMS;
+        }
+    } else if (need > e->ws_size) {
         if (e->ws) { (void)hipFree(e->ws); e->ws = nullptr; e->ws_size = 0; }
         hipError_t st = hipMalloc(&e->ws, need);
         if (st != hipSuccess) {
@@ -635,19 +684,29 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
         }
         e->ws_size = need;
     }
-    if (table_bytes > e->pinned_size) {
-        if (e->pinned) { (void)hipHostFree(e->pinned); e->pinned = nullptr; e->pinned_size = 0; }
-        hipError_t st = hipHostMalloc(&e->pinned, table_bytes, hipHostMallocDefault);
-        if (st != hipSuccess) { set_err("pinned staging: %s", hipGetErrorString(st)); return QA_STATUS_OOM; }
-        e->pinned_size = table_bytes;
+    // the tables, laid out as in the workspace: in the pinned staging buffer
+    // (grown on demand), or with a fixed workspace in pageable host memory
+    std::vector<char> host_tables;
+    char* tables = nullptr;
+    if (fixed) {
+        host_tables.resize(table_bytes);
+        tables = host_tables.data();
+    } else {
+        if (table_bytes > e->pinned_size) {
+            if (e->pinned) { (void)hipHostFree(e->pinned); e->pinned = nullptr; e->pinned_size = 0; }
+            hipError_t st = hipHostMalloc(&e->pinned, table_bytes, hipHostMallocDefault);
+            if (st != hipSuccess) { set_err("pinned staging: %s", hipGetErrorString(st)); return QA_STATUS_OOM; }
+            e->pinned_size = table_bytes;
+        }
+        tables = e->pinned;
     }
-    memcpy(e->pinned + o_clips, clips.data(), clips.size() * sizeof(qa::ClipInfo));
-    memcpy(e->pinned + o_tiles, tiles.data(), tiles.size() * sizeof(qa::FrontTile));
-    memcpy(e->pinned + o_chunks, chunks.data(), chunks.size() * sizeof(qa::ChunkInfo));
-    memcpy(e->pinned + o_src, tok_src.data(), tok_src.size() * 4);
-    memcpy(e->pinned + o_cu, cu.data(), cu.size() * 4);
+    memcpy(tables + o_clips, clips.data(), clips.size() * sizeof(qa::ClipInfo));
+    memcpy(tables + o_tiles, tiles.data(), tiles.size() * sizeof(qa::FrontTile));
+    memcpy(tables + o_chunks, chunks.data(), chunks.size() * sizeof(qa::ChunkInfo));
+    memcpy(tables + o_src, tok_src.data(), tok_src.size() * 4);
+    memcpy(tables + o_cu, cu.data(), cu.size() * 4);
 
-    char* ws = e->ws;
+    char* ws = fixed ? fixed->base : e->ws;
     auto P = [&](size_t o) { return ws + o; };
     const auto* d_clips = reinterpret_cast<const qa::ClipInfo*>(P(o_clips));
     const auto* d_tiles = reinterpret_cast<const qa::FrontTile*>(P(o_tiles));
@@ -665,8 +724,8 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     T* qkv = reinterpret_cast<T*>(P(o_qkv));
     T* att = reinterpret_cast<T*>(P(o_att));
     T* u = reinterpret_cast<T*>(P(o_u));
-    float* tstem = e->taps ? reinterpret_cast<float*>(P(o_tstem)) : nullptr;
-    float* tl0 = e->taps ? reinterpret_cast<float*>(P(o_tl0)) : nullptr;
+    float* tstem = taps ? reinterpret_cast<float*>(P(o_tstem)) : nullptr;
+    float* tl0 = taps ? reinterpret_cast<float*>(P(o_tl0)) : nullptr;
     float* part = part_elems ? reinterpret_cast<float*>(P(o_part)) : nullptr;
     hipStream_t s = e->stream;
 
@@ -674,7 +733,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     e->prof_cur.clear();
     size_t ev_next = 0;
     auto launch = [&](const char* label, auto&& fn) -> hipError_t {
-        if (!e->profiling || (!e->prof_only.empty() && e->prof_only != label)) return fn();
+        if (!profiling || (!e->prof_only.empty() && e->prof_only != label)) return fn();
         while (e->ev_pool.size() < ev_next + 2) {
             hipEvent_t ev;
             hipError_t st = hipEventCreate(&ev);
@@ -698,7 +757,9 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
         }                                                                                   \
     } while (0)
 
-    QA_LAUNCH("tables", hipMemcpyAsync(ws, e->pinned, table_bytes, hipMemcpyHostToDevice, s));
+    // (from pageable memory the copy is staged before the call returns;
+    // host_tables outlives the stream synchronisation below either way)
+    QA_LAUNCH("tables", hipMemcpyAsync(ws, tables, table_bytes, hipMemcpyHostToDevice, s));
     QA_LAUNCH("init", qa::init_flags(s, key, n_clips, flag));
     QA_LAUNCH("frontend", qa::frontend(s, pcm, d_clips, d_tiles, n_tiles, e->W<uint4>(e->basis), e->W<float>(e->melw),
                                        e->W<int>(e->melb0), logmel, key, flag));
@@ -716,7 +777,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2, n_chunks, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b), c3, true, false));
     QA_LAUNCH("conv_out", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), x, nullptr,
                                           part, part_elems));
-    if (e->taps)
+    if (taps)
         QA_LAUNCH("tap_stem", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), tl0, tstem,
                                               part, part_elems));
     for (int l = 0; l < d.n_layers; ++l) {
@@ -730,7 +791,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
         QA_LAUNCH("fc1", qa::gemm_bias<T>(s, h, n_tok, D, e->W<T>(lw.fc1_w), F, e->W<float>(lw.fc1_b), u, true));
         QA_LAUNCH("fc2", qa::gemm_bias_resid<T>(s, u, n_tok, F, e->W<T>(lw.fc2_w), D, e->W<float>(lw.fc2_b), x,
                                                 part, part_elems));
-        if (l == 0 && e->taps)
+        if (l == 0 && taps)
             QA_LAUNCH("tap_layer0", hipMemcpyAsync(tl0, x, (size_t)n_tok * D * 4, hipMemcpyDeviceToDevice, s));
     }
     QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(e->post_ln_w), e->W<float>(e->post_ln_b), h));
@@ -743,7 +804,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
         set_err("stream synchronize: %s", hipGetErrorString(st));
         return QA_STATUS_ENCODE_FAILED;
     }
-    if (e->profiling) {
+    if (profiling) {
         for (const Profile& p : e->prof_cur) {
             float ms = 0.f;
             if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
@@ -753,7 +814,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
             }
         }
     }
-    if (e->taps) {
+    if (taps) {
         e->tap_frames = n_frames;
         e->tap_tokens = n_tok;
         e->tap_logmel = logmel;
@@ -769,7 +830,9 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
 
 }  // namespace
 
-QA_API int qa_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_clips, float* out) {
+namespace {
+
+int encode_entry(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_clips, float* out, bool noalloc) {
     if (!e) { set_err("encoder is NULL"); return QA_STATUS_INVALID_PARAMS; }
     if (n_clips < 0) { set_err("n_clips < 0"); return QA_STATUS_INVALID_PARAMS; }
     if (n_clips > 0 && !lengths) { set_err("lengths is NULL"); return QA_STATUS_INVALID_PARAMS; }
@@ -795,6 +858,29 @@ QA_API int qa_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, in
     }
     hipError_t st = hipSetDevice(e->device);
     if (st != hipSuccess) { set_err("hipSetDevice: %s", hipGetErrorString(st)); return QA_STATUS_ENCODE_FAILED; }
-    if (e->d.dtype == QA_DTYPE_BF16) return run_encode<bf16>(e, pcm, lengths, n_clips, out);
-    return run_encode<float>(e, pcm, lengths, n_clips, out);
+    FixedWorkspace fw{nullptr, 0};
+    if (noalloc) {
+        fw.base = static_cast<char*>(scratch_address(e->device));
+        if (!fw.base) {
+            std::lock_guard<std::mutex> lock(g_scratch_mu);
+            set_err("no scratch array on device %d: %s", e->device,
+                    e->device >= 0 && e->device < kMaxDevices ? hipGetErrorString(g_scratch_err[e->device])
+                                                              : "device id out of range");
+            return QA_STATUS_ENCODE_FAILED;
+        }
+        fw.bytes = kScratchBytes;
+    }
+    const FixedWorkspace* f = noalloc ? &fw : nullptr;
+    if (e->d.dtype == QA_DTYPE_BF16) return run_encode<bf16>(e, pcm, lengths, n_clips, out, f);
+    return run_encode<float>(e, pcm, lengths, n_clips, out, f);
+}
+
+}  // namespace
+
+QA_API int qa_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_clips, float* out) {
+    return encode_entry(e, pcm, lengths, n_clips, out, false);
+}
+
+QA_API int qa_encode_noalloc(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_clips, float* out) {
+    return encode_entry(e, pcm, lengths, n_clips, out, true);
 }

@@ -161,6 +161,26 @@ int qa_encoder_set_stream(qa_encoder *e, void *hip_stream);
  * Calls on one handle must not overlap. */
 int qa_encode(qa_encoder *e, const float *pcm, const int64_t *lengths, int n_clips, float *out);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qa_encode with the same
+ * arguments, kernels and results, but its workspace is a fixed device array
+ * of QA_NOALLOC_SCRATCH_BYTES bytes per GPU, part of the library's device
+ * image (each GPU the library runs on holds one until the process ends; its
+ * address is taken once per device by qa_encoder_create).  The call makes no
+ * device, pinned-host or event allocation: the small planning tables go to
+ * the device from pageable host memory.  A batch whose workspace exceeds the
+ * array is refused with INVALID_PARAMS before any device work (a 30 s clip of
+ * the 0.6B shape needs about 136 MiB; the workspace grows with the total
+ * audio: roughly 4.6 MiB per second at 480 stem channels).  Taps and
+ * profiling events are not recorded by this call (qa_encoder_tap then fails
+ * until the next qa_encode with taps).  Every call on one GPU, through any
+ * handle, shares that GPU's array and overwrites it: calls that overlap on
+ * one GPU (other streams, other threads, other handles) race and must be
+ * serialised by the caller.  Returns as qa_encode; ENCODE_FAILED if the
+ * array's device address could not be obtained. */
+#define QA_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
+int qa_encode_noalloc(qa_encoder *e, const float *pcm, const int64_t *lengths, int n_clips, float *out);
+
 /* Keep stage outputs of later qa_encode calls for qa_encoder_tap (costs one
  * extra conv_out GEMM and a copy per call).  enable: 0 or 1. */
 int qa_encoder_enable_taps(qa_encoder *e, int enable);
