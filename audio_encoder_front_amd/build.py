@@ -1,9 +1,10 @@
-"""Build libqa_encoder.so (gfx950) in-tree with hipcc.
+"""Build libqa_encoder.so and libqa_probe.so (gfx950) in-tree with hipcc.
 
     python -m audio_encoder_front_amd.build          # or build() from Python
 
-Each source compiles to an object under _build/ (in parallel), then one
-shared library exporting only the qa_* symbols is linked next to this file.
+Each source compiles to an object under _build/ (in parallel), then the
+encoder library (exporting only the qa_* symbols) and the probe library the
+benchmark loads are linked next to this file.
 """
 from __future__ import annotations
 
@@ -19,6 +20,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqa_encoder.so")
 SOURCES = ["frontend.hip", "stem.hip", "gemm.hip", "norm_attn.hip", "resample.hip", "thinker.hip", "encoder.cpp",
            "thinker_host.cpp"]
+# the ceiling probes the benchmark runs beside the encoder (not the encoder's path)
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libqa_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [
@@ -40,19 +44,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -25,6 +25,11 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+def log(msg: str) -> None:
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def plan_counts(lengths, chunk_tok=13, window_chunks=8):
     """Integer bookkeeping of the batch: chunks (tails padded to 100 frames
     count as full chunks of stem work), tokens, window sizes, frames."""
@@ -41,15 +46,29 @@ def plan_counts(lengths, chunk_tok=13, window_chunks=8):
     return chunks, tokens, frames, windows
 
 
+# The front end's DFT per STFT frame: 400 windowed samples against 201 cos and
+# 201 sin basis rows, 2 * 400 * 402 = 321,600 flops of fp32 work (the sparse
+# Slaney mel adds 2 * 394, on the VALU).  The kernel runs it on the bf16 MFMA
+# as six products of exact three-part bf16 splits, on the MFMA-padded shape
+# of 416 samples (13 K blocks of 32) x 208 bins (13 tiles of 16) x cos, sin:
+# 6 * 2 * 416 * 208 * 2 = 2,076,672 bf16 MFMA flops per frame, the figure
+# its roofline is stated against (the bf16 dense peak).
+FRONT_FP32_FLOPS = 2 * 400 * 402
+FRONT_BF16_EXEC_FLOPS = 6 * 2 * 416 * 208 * 2
+
+
 def kernel_work(d, lengths):
     """Algorithmic work per launch of each labelled kernel: (flops, bytes,
     peak label).  Flops count dense MACs as 2; bytes count compulsory HBM
-    traffic (operands read once, results written once)."""
+    traffic (operands read once, results written once).  The front end's
+    flops are the bf16 MFMA flops it executes (FRONT_BF16_EXEC_FLOPS per
+    frame, the final STFT frame of each clip included)."""
     C, D, F, O, H = d.conv_channels, d.d_model, d.ffn_dim, d.output_dim, d.n_heads
     ch, T, fr, wins = plan_counts(lengths, window_chunks=d.window_chunks)
     e = 2 if d.dtype == "bf16" else 4
+    fr_all = fr + sum(1 for n in lengths if n)
     work = {
-        "frontend": (fr * (2 * 400 * 400 + 2 * 201 * 128), sum(lengths) * 4 + fr * 128 * 4, "fp32"),
+        "frontend": (fr_all * FRONT_BF16_EXEC_FLOPS, sum(lengths) * 4 + fr * 128 * 4, "bf16"),
         "conv2": (2 * ch * 800 * C * 9 * C, ch * 64 * 50 * C * e + ch * 800 * C * e + 9 * C * C * e, "bf16"),
         "conv3": (2 * ch * 208 * C * 9 * C, ch * 800 * C * e + ch * 208 * C * e + 9 * C * C * e, "bf16"),
         "conv_out": (2 * T * 16 * C * D, T * 16 * C * e + 16 * C * D * e + T * D * 4, "bf16"),
@@ -220,25 +239,140 @@ def full_input_bench(dev, wl, weights, n_clips: int = 40, seconds: int = 30, ste
                           "gbs": round(b / (att_avg * 1e-3) / 1e9, 1)}}
 
 
-def cpu_baseline(wl, seconds: float):
-    """The fp64 oracle on the first `seconds` of the workload's first clip."""
+def cpu_baseline(wl, clips, weights, seconds: float = 0.0):
+    """The fp64 oracle (as it stands) on the workload's clips, on the host's
+    cores: per clip, its log-mel once, then oracle.encode_clip over groups of
+    windows on one thread per usable core (one BLAS thread each; NumPy
+    releases the GIL in its matmuls).  seconds > 0 takes only the first
+    `seconds` of the first clip."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_info, threadpool_limits
     import oracle as O
-    import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
-    except Exception:  # pragma: no cover
-        threads, blas = os.cpu_count(), "?"
-    clip = synth.make_audio(wl)[0][: int(seconds * 16000)]
-    w = synth.make_weights(wl.dims, wl.weight_seed)
+    cores = len(os.sched_getaffinity(0))
+    blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
+    if seconds > 0:
+        clips = [clips[0][: int(seconds * 16000)]]
+    W = O.as_f64(weights)
+    d = wl.dims
     t0 = time.perf_counter()
-    out = O.encode([clip], w, wl.dims.n_layers, wl.dims.n_heads, window_chunks=wl.dims.window_chunks)
+    tokens = 0
+    with threadpool_limits(1), ThreadPoolExecutor(cores) as ex:
+        for clip in clips:
+            x = np.asarray(clip, dtype=np.float64)
+            nt = O.clip_num_tokens(len(x))
+            if nt == 0:
+                continue
+            mel = O.log_mel(x)
+            wins = list(range(len(O.window_bounds(nt, 13 * d.window_chunks))))
+            groups = [g for g in (wins[i::cores] for i in range(cores)) if g]
+            outs = list(ex.map(lambda g: O.encode_clip(x, W, d.n_layers, d.n_heads, window_chunks=d.window_chunks,
+                                                       windows=g, mel=mel), groups))
+            tokens += sum(v.shape[0] for o in outs for v in o.values())
     dt = time.perf_counter() - t0
-    return {"value": len(clip) / 16000.0 / dt, "unit": "audio-s/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {seconds:g} s of the clip as one clip ({out.shape[0]} tokens), fp64 NumPy "
-                      f"({blas}), {dt:.1f} s wall"}
+    audio = sum(len(c) for c in clips) / 16000.0
+    what = f"first {seconds:g} s of the first clip" if seconds > 0 else f"the whole workload ({len(clips)} clip(s))"
+    return {"value": audio / dt, "unit": "audio-s/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}: {audio:g} s of audio, {tokens} tokens; fp64 NumPy ({blas}), the windows of a "
+                      f"clip split over {cores} threads with one BLAS thread each; {dt:.1f} s wall"}
+
+
+def vendor_block(dev, d, tokens: int, chunks: int, reps: int = 10):
+    """The same contractions through the vendor libraries via torch (context,
+    not part of `value`): the four encoder-layer GEMMs as torch.nn.functional
+    .linear in bf16 (hipBLASLt; bias only, no fused GELU or residual) and conv2
+    as conv2d in bf16 channels-last (MIOpen; bias only, no GELU), on random
+    operands of the workload's shapes; median of `reps` timed calls."""
+    import torch
+    import torch.nn.functional as Fn
+    g = torch.Generator(device=dev).manual_seed(7)
+    D, F, C = d.d_model, d.ffn_dim, d.conv_channels
+    s = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def med(fn):
+        fn()
+        t = []
+        for _ in range(reps):
+            e0.record(s)
+            fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return sorted(t)[len(t) // 2]
+
+    def rnd(*shape):
+        return (torch.randn(*shape, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+
+    res = {}
+    for name, (k, n) in {"qkv": (D, 3 * D), "o_proj": (D, D), "fc1": (D, F), "fc2": (F, D)}.items():
+        x, w, b = rnd(tokens, k), rnd(n, k), rnd(n)
+        ms = med(lambda: Fn.linear(x, w, b))
+        res[name] = {"avg_ms": round(ms, 4), "tflops": round(2.0 * tokens * k * n / (ms * 1e-3) / 1e12, 1)}
+        del x, w, b
+    x = rnd(chunks, C, 64, 50).contiguous(memory_format=torch.channels_last)
+    w = rnd(C, C, 3, 3).contiguous(memory_format=torch.channels_last)
+    b = rnd(C)
+    ms = med(lambda: Fn.conv2d(x, w, b, stride=2, padding=1))
+    res["conv2"] = {"avg_ms": round(ms, 4), "tflops": round(2.0 * chunks * 800 * C * 9 * C / (ms * 1e-3) / 1e12, 1)}
+    del x, w, b
+    torch.cuda.empty_cache()
+    res["note"] = ("torch bf16 linear (hipBLASLt) and channels-last conv2d (MIOpen), bias only; "
+                   "the encoder's own kernels also fuse GELU, the fp32 residual and the bf16 conversion")
+    return res
+
+
+def workload_block(dev, name, weights=None, steps: int = 10, warmup: int = 3):
+    """Throughput of another benchmark workload through the same qa_encode
+    (not part of `value`), with the roofline fraction of its dominant kernel
+    from one step with events around every launch."""
+    import numpy as np
+    import torch
+    import audio_encoder_front_amd as qa
+    import synth
+    wl = synth.WORKLOADS[name]
+    clips = synth.make_audio(wl)
+    lengths = [len(c) for c in clips]
+    if weights is None:
+        weights = synth.make_weights(wl.dims, wl.weight_seed)
+    enc = qa.qa_encoder_create(weights, wl.dims)
+    stream = torch.cuda.current_stream(dev)
+    qa.qa_encoder_set_stream(enc, stream)
+    pcm = torch.from_numpy(np.concatenate(clips)).to(dev)
+    T = sum(qa.qa_encode_num_tokens(n) for n in lengths)
+    out = torch.empty((T, wl.dims.output_dim), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        qa.qa_encode(enc, pcm, lengths, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        qa.qa_encode(enc, pcm, lengths, out)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    qa.qa_encoder_set_profiling(enc, True)
+    qa.qa_encode(enc, pcm, lengths, out)
+    torch.cuda.synchronize()
+    times = qa.qa_encoder_kernel_times(enc)
+    qa.qa_encoder_set_profiling(enc, False)
+    enc.free()
+    work, (ch, _, fr, wins) = kernel_work(wl.dims, lengths)
+    dom = max((l for l in times if l in work), key=lambda l: times[l][0])
+    f, b, kind = work[dom]
+    ms, cnt = times[dom]
+    avg_s = ms / max(cnt, 1) * 1e-3
+    total_flops = sum(work[l][0] * c for l, (_, c) in times.items() if l in work and l != "frontend")
+    audio = sum(lengths) / 16000.0
+    blk = {"workload": f"{name}: {wl.description}", "audio_s": round(audio, 2), "tokens": T, "windows": len(wins),
+           "audio_s_per_s": round(audio / dt, 1), "tokens_per_s": round(T / dt, 1), "ms_per_step": round(dt * 1e3, 4),
+           "mfma_util_pct": round(100.0 * total_flops / dt / (PEAK_BF16_TFLOPS * 1e12), 2),
+           "dominant": {"kernel": dom, "avg_ms": round(avg_s * 1e3, 5), "launches": int(cnt),
+                        "share_of_step": round(ms / (dt * 1e3), 3)}}
+    if kind == "hbm":
+        blk["dominant"].update(bound="hbm", gbs=round(b / avg_s / 1e9, 1), frac=round(b / avg_s / 1e9 / PEAK_HBM_GBS, 4))
+    else:
+        blk["dominant"].update(bound="mfma", tflops=round(f / avg_s / 1e12, 1),
+                               frac=round(f / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4))
+    return blk
 
 
 def main():
@@ -247,10 +381,15 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="b17_20m")
-    ap.add_argument("--cpu-sample-s", type=float, default=240.0)
+    ap.add_argument("--cpu-sample-s", type=float, default=0.0,
+                    help="oracle on the first N s of the first clip only (default 0: the whole workload)")
+    ap.add_argument("--other-workloads", default="b06_1,b06_32,b17_16",
+                    help="comma-separated workloads reported beside the main one ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-thinker", action="store_true", help="skip the Thinker-prefill line")
     ap.add_argument("--no-full-input", action="store_true", help="skip the full-input attention line")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time the layer GEMMs and conv2 through torch's vendor libraries (context)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -304,7 +443,10 @@ def main():
 
     audio_s = sum(lengths) / 16000.0
     ms_step = dt / args.steps * 1e3
-    total_flops = sum(work[l][0] * cnt for l, (_, cnt) in times.items() if l in work) / prof_steps
+    # algorithmic flops of the step (the front end's bf16 split products are
+    # not the method's work: it counts with its fp32 DFT flops)
+    total_flops = sum(work[l][0] * cnt for l, (_, cnt) in times.items() if l in work and l != "frontend") / prof_steps
+    total_flops += n_frames * FRONT_FP32_FLOPS
     kernels = {}
     for label, (ms, cnt) in sorted(times.items()):
         avg = ms / max(cnt, 1)
@@ -315,7 +457,14 @@ def main():
                 ent["tflops"] = round(f / (avg * 1e-3) / 1e12, 2)
             if b:
                 ent["gbs"] = round(b / (avg * 1e-3) / 1e9, 1)
+            if kind == "hbm":
+                ent["frac_of_hbm_peak"] = round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            elif f:
+                ent["frac_of_bf16_peak"] = round(f / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
         kernels[label] = ent
+    kernels["frontend"]["note"] = (f"tflops = executed bf16 MFMA flops ({FRONT_BF16_EXEC_FLOPS} per frame: six "
+                                   f"split products on the padded 416 x 208 x 2 DFT) against the bf16 peak; the "
+                                   f"DFT's fp32 work is {FRONT_FP32_FLOPS} flops per frame")
     f, b, kind = work[dom]
     avg_s = dom_ms / max(dom_cnt, 1) * 1e-3
     if kind == "hbm":
@@ -351,17 +500,52 @@ def main():
         "kernels_note": f"per-kernel table from {prof_steps} separate steps with events around every launch; "
                         "the timed steps carry events only around the dominant kernel",
     }
+    log(f"{wl.name}: {res['value']} audio-s/s, {ms_step:.3f} ms per step")
+    # ceilings measured on this GPU in this run (register-only MFMA loop, HBM streaming)
+    try:
+        from audio_encoder_front_amd import probe
+        res["ceilings"] = probe.measure(dev)
+        c = res["ceilings"]
+        meas = c["mfma_bf16_random_tflops"] if roof["unit"] == "TFLOP/s" else c["hbm_read_gbs"]
+        roof["measured_ceiling"] = meas
+        roof["frac_of_measured_ceiling"] = roof["achieved"] / meas
+        for ent in kernels.values():
+            if "frac_of_bf16_peak" in ent:
+                ent["frac_of_measured_mfma"] = round(ent["tflops"] / c["mfma_bf16_random_tflops"], 4)
+            elif "frac_of_hbm_peak" in ent:
+                ent["frac_of_measured_hbm"] = round(ent["gbs"] / c["hbm_read_gbs"], 4)
+        res["ceilings"]["note"] = ("bf16 MFMA: register-only loop of 16x16x32 MFMAs with random full-mantissa "
+                                   "operands (and all-ones operands); HBM: 1 GiB streaming read and copy; best of 5")
+        log(f"ceilings: {c}")
+    except (ImportError, OSError, RuntimeError) as ex:   # the probe library is optional for the encoder
+        res["ceilings"] = {"error": str(ex)}
     res["resample"] = resample_bench(dev)
+    log("resampler done")
     if not args.no_full_input and wl.dims.window_chunks:
         res["full_input"] = full_input_bench(dev, wl, weights)
-    del weights
+        log("full-input attention done")
+    others = [w for w in args.other_workloads.split(",") if w and w != wl.name]
+    if others:
+        res["other_workloads"] = {}
+        for name in others:
+            same = synth.WORKLOADS[name].dims == wl.dims and synth.WORKLOADS[name].weight_seed == wl.weight_seed
+            res["other_workloads"][name] = workload_block(dev, name, weights if same else None)
+            torch.cuda.empty_cache()
+            log(f"{name}: {res['other_workloads'][name]['audio_s_per_s']} audio-s/s")
     if not args.no_thinker:
         res["thinker_prefill"] = thinker_bench(dev, out, wl)
+        log("thinker prefill done")
+    if args.vendor:
+        res["vendor"] = vendor_block(dev, wl.dims, T, n_chunks)
+        log(f"vendor libraries: {res['vendor']}")
     if args.calibrate_copy:
         copy_calibration()
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_s)
     enc.free()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (the oracle on the host) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, clips, weights, args.cpu_sample_s)
+        log(f"cpu baseline: {res['cpu_baseline']['sample']}")
+    del weights
     print(json.dumps(res), flush=True)
 
 

@@ -141,3 +141,18 @@ def test_binding_checks_lengths_and_tap_buffers_before_the_library(qa):
     for dst in (torch.zeros(8), torch.zeros(8, dtype=torch.bfloat16)):
         with pytest.raises(qa.QAError):
             qa.qa_encoder_tap(enc, qa._binding.QA_TAP_LOG_MEL, dst)
+
+
+def test_probe_library_exports_its_header():
+    """libqa_probe.so (the benchmark's ceiling probes) exports what
+    include/qa_probe.h declares."""
+    from audio_encoder_front_amd import probe
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qa_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(qa_[a-z_0-9]+)\s*\(", src)))
+    assert len(names) == 4
+    lib = probe._load()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.qa_probe_mfma_flops(2, 3) == 2 * 4 * 3 * 32 * 16 * 16 * 32 * 2
+    assert lib.qa_probe_mfma_bf16(None, 0, 1, 1, None) == -1
+    assert lib.qa_probe_read(None, None, 1024, None) == -1
