@@ -15,6 +15,8 @@
 #include "qa_device.h"
 #include "qa_kernels.h"
 
+#include <type_traits>
+
 namespace qa {
 
 // ------------------------------------------------------------ LayerNorm
@@ -316,6 +318,163 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     }
 }
 
+// bf16 windows, two heads per workgroup (four waves each): K and V go
+// global -> LDS by direct-to-LDS loads (no register round trip), both
+// row-major with their 16-byte chunks XOR-swizzled per row, and the P.V
+// operand V^T comes from LDS transpose reads (ds_read_b64_tr_b16: within each
+// 16-lane group the 4-element reads of lanes 4 r .. 4 r + 3 form row r of a
+// 4 x 16 matrix and lane i receives column i, so two reads give a lane one
+// head dimension at 4 + 4 keys).  The two heads of a window read neighbouring
+// 128-byte pieces of the same token rows.  Key slots are those of
+// attention_kernel (slots 0..3 of a 32-key step: keys 4 g + r, slots 4..7:
+// 16 + 4 g + r), so the results are identical to it.
+__device__ __forceinline__ int vchunk_swz(int j) { return 2 * (j & 3); }   // keeps chunk pairs adjacent
+
+typedef short lds_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) lds_s16x4 lds_s16x4_p;
+__device__ __forceinline__ uint2 lds_tr_read(const char* p) {
+    const lds_s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p*)p);
+    return __builtin_bit_cast(uint2, v);
+}
+
+constexpr int kAttnHpw = 2;                      // heads per workgroup of attention_dma_kernel
+
+template <int KT>
+__global__ __launch_bounds__(256 * kAttnHpw) void attention_dma_kernel(const bf16* __restrict__ qkv,
+                                                                       const int* __restrict__ cu, int n_heads, int d,
+                                                                       bf16* __restrict__ out) {
+    constexpr int ROWS = KT * 16;                  // keys held in LDS
+    constexpr int RB = kHd * 2;                    // bytes per K / V row
+    constexpr int BLK = ROWS * RB;                 // bytes per K or V block of one head
+    constexpr int NLD = BLK / 1024;                // 1 KB direct-to-LDS loads per block (8 rows each)
+    constexpr int KBN = kHd * 2 / 64;              // 64-byte MFMA K blocks per head row
+    static_assert(ROWS % 8 == 0, "rows per load");
+    __shared__ __align__(1024) char smem_all[kAttnHpw * 2 * BLK];
+    const int hw = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);   // head within the workgroup
+    const char* ks = smem_all + hw * 2 * BLK;
+    const char* vs = ks + BLK;
+    const int hg = n_heads / kAttnHpw;
+    const int win = blockIdx.x / hg, h = (blockIdx.x % hg) * kAttnHpw + hw;
+    const int s0 = cu[win], n = cu[win + 1] - s0;
+    const int tid = threadIdx.x & 255;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fr = lane & 15, fg = lane >> 4;
+    const int nt = (n + 15) >> 4;
+    const size_t ld = 3 * (size_t)d;
+    const unsigned row_bytes = (unsigned)(ld * 2);
+
+    // query fragments (B operand: lane holds query row fr, K chunk fg of each block)
+    auto load_q = [&](int qt, uint4* qf) {
+        const int q = qt * 16 + fr;
+        const bf16* row = qkv + (size_t)(s0 + q) * ld + h * kHd + fg * 8;
+#pragma unroll
+        for (int kb = 0; kb < KBN; ++kb) qf[kb] = q < n ? ld16(row + kb * 32) : zero16();
+    };
+    uint4 qf[KBN];
+    if (wave < nt) load_q(wave, qf);
+
+    // K and V rows of this head: load q of a block fills rows 8 q .. 8 q + 7,
+    // lane l row 8 q + l / 8 at LDS chunk l % 8, which holds source chunk
+    // (l % 8) ^ swizzle(row); rows at or past n read zeros (buffer range).
+    {
+        const i32x4 rk = buffer_rsrc(qkv + (size_t)s0 * ld + d + h * kHd, (uint64_t)n * row_bytes);
+        const i32x4 rv = buffer_rsrc(qkv + (size_t)s0 * ld + 2 * d + h * kHd, (uint64_t)n * row_bytes);
+        const unsigned lds0 = (unsigned)(uintptr_t)(lds_void*)ks;
+        const int lr = lane >> 3, p = lane & 7;
+#pragma unroll
+        for (int q = wave; q < 2 * NLD; q += 4) {  // wave-uniform: K loads, then V loads
+            if (q < NLD) {
+                const int row = 8 * q + lr;
+                dma16_buf(rk, row < n ? (unsigned)row * row_bytes + (unsigned)((p ^ (row & 7)) << 4) : kOobOffset,
+                          lds0 + q * 1024);
+            } else {
+                const int row = 8 * (q - NLD) + lr;
+                dma16_buf(rv, row < n ? (unsigned)row * row_bytes + (unsigned)((p ^ vchunk_swz(row)) << 4) : kOobOffset,
+                          lds0 + BLK + (q - NLD) * 1024);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this wave's queries and K / V loads
+    __syncthreads();
+
+    const float sc = 0.125f * 1.4426950408889634f; // 1/sqrt(64) * log2(e)
+    const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;   // transpose-read source row / 8-byte column
+    for (int qt = wave; qt < nt; qt += 4) {
+        f32x4 sacc[8];
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KBN; ++kb) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {      // rows past n are zeros, masked below
+                const int row = kt * 16 + fr;
+                const uint4 kf = ld16(ks + row * RB + (((4 * kb + fg) ^ (row & 7)) << 4));
+                mfma_kblock(bf16(), kf, qf[kb], sacc[kt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (qt + 4 < nt) load_q(qt + 4, qf);       // next tile's queries, in flight during softmax and P.V
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            if (kt * 16 + 16 > n) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (kt * 16 + 4 * fg + r >= n) sacc[kt][r] = -INFINITY;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float off = -mx * sc;
+        float sum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sc, off));
+                sacc[kt][r] = pr;
+                sum += pr;
+            }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        f32x4 o[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // P.V per 32-key step: rows j0 and j0 + 16 (j0 = 32 st + 4 g + tr_r) of V
+#pragma unroll
+        for (int st = 0; st < (KT + 1) / 2; ++st) {
+            bf16x8 pb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pb[r] = (bf16)sacc[2 * st][r];
+                pb[4 + r] = 2 * st + 1 < KT ? (bf16)sacc[2 * st + 1][r] : (bf16)0.f;
+            }
+            const int j0 = 32 * st + 4 * fg + tr_r, j1 = j0 + 16;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const int c = 2 * dt + (tr_c >> 1), half = (tr_c & 1) * 8;
+                const uint2 lo = lds_tr_read(vs + j0 * RB + ((c ^ vchunk_swz(j0)) << 4) + half);
+                // an odd key-tile count leaves the last step's second tile outside the LDS rows
+                const uint2 hi = 2 * st + 1 < KT ? lds_tr_read(vs + j1 * RB + ((c ^ vchunk_swz(j1)) << 4) + half)
+                                                 : make_uint2(0u, 0u);
+                const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[dt], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int q = qt * 16 + fr;
+        if (q < n) {
+            const float inv = 1.0f / sum;
+            bf16* orow = out + (size_t)(s0 + q) * d + h * kHd;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                store4(orow + dt * 16 + 4 * fg, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+        }
+    }
+}
+
 // Segments longer than 128 tokens (full-input attention over a whole clip):
 // one workgroup per (segment, head, block of QB queries): 128 queries in bf16
 // with two 16-query tiles per wave (each K / V fragment read from LDS feeds
@@ -588,7 +747,14 @@ template <typename T>
 hipError_t attention(hipStream_t s, const T* qkv, const int* cu_seqlens, int n_windows, int n_heads,
                      int d, int max_len, T* out) {
     if (n_windows <= 0) return hipSuccess;
-    if (max_len <= 112) {          // every window fits 7 key tiles (104-token windows)
+    if (std::is_same<T, bf16>::value && n_heads % kAttnHpw == 0 && max_len <= kMaxWindow) {
+        // bf16, an even number of heads: direct-to-LDS kernel, two heads per workgroup
+        const unsigned blocks = (unsigned)(n_windows * (n_heads / kAttnHpw));
+        const bf16* q = reinterpret_cast<const bf16*>(qkv);
+        bf16* o = reinterpret_cast<bf16*>(out);
+        if (max_len <= 112) attention_dma_kernel<7><<<blocks, 256 * kAttnHpw, 0, s>>>(q, cu_seqlens, n_heads, d, o);
+        else attention_dma_kernel<kMaxWindow / 16><<<blocks, 256 * kAttnHpw, 0, s>>>(q, cu_seqlens, n_heads, d, o);
+    } else if (max_len <= 112) {          // every window fits 7 key tiles (104-token windows)
         attention_kernel<T, 7><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);
     } else if (max_len <= kMaxWindow) {
         attention_kernel<T, kMaxWindow / 16><<<n_windows * n_heads, 256, 0, s>>>(qkv, cu_seqlens, n_heads, d, out);

@@ -107,6 +107,47 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
 
+// ---- direct-to-LDS loads (global -> LDS without a register round trip)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS loads written as inline asm: the compiler's wait-count pass
+// cannot tell the LDS stages apart and would otherwise wait for the
+// in-flight loads of later stages before every LDS read of stage k.
+// Completion is awaited explicitly (s_waitcnt vmcnt(n), leaving the n loads
+// of the stage two ahead in flight) before the barrier that publishes a
+// stage.  M0 carries the wave's LDS destination; no other code in these
+// kernels uses M0.
+//
+// Two forms.  buffer_load_dwordx4 ... lds reads through a buffer resource
+// (base and size in four SGPRs) at a 32-bit lane offset: one VGPR per load
+// and no 64-bit address arithmetic, and any offset at or past the resource
+// size reads zeros, which covers ragged rows and conv padding for free.  The
+// loaders that can keep their per-workgroup range under 4 GB (dense rows, conv
+// chunks) use it; the row-gather loader uses global_load_lds_dwordx4 with
+// 64-bit addresses and a zero block.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr unsigned kOobOffset = 0xFFFFFFF0u;     // >= every resource size below: reads zeros
+
+__device__ __forceinline__ void dma16(const void* src, unsigned lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "m0");
+}
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, unsigned voff, unsigned lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff),
+                 "s"(rsrc) : "m0");
+}
+// Raw buffer resource (stride 0) over [base, base + bytes), bytes clamped
+// below kOobOffset; the fourth word is the gfx9 raw-buffer format.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint64_t bytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const unsigned n = bytes < 0xFFFFFF00ull ? (unsigned)bytes : 0xFFFFFF00u;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)n);
+    r[3] = 0x00020000;
+    return r;
+}
+
 // Order-preserving int key of a float, for atomicMax over floats.
 __device__ __forceinline__ int float_key(float f) {
     int i = __float_as_int(f);
