@@ -233,11 +233,12 @@ def test_b17_packed_16_clips_every_window(b17):
     assert len(rows) >= 8
 
 
-@pytest.mark.parametrize("base,window_chunks", [("tiny", 9), ("tiny", 1), ("b06", 9)])
+@pytest.mark.parametrize("base,window_chunks", [("tiny", 9), ("tiny", 1), ("b06", 9), ("b06", 1)])
 def test_other_window_sizes(base, window_chunks):
-    """Attention windows of 9 chunks (117 tokens: the 8-key-tile kernel, whose
-    last P.V step is a full 32-key step) and of 1 chunk (13 tokens: mostly
-    masked key tiles), fp32 miniature and 0.6B bf16."""
+    """Attention windows of 9 chunks (117 tokens: 8 key tiles, whose last P.V
+    step is a full 32-key step) and of 1 chunk (13 tokens: one query tile,
+    mostly zero key rows), fp32 miniature (one head per workgroup) and 0.6B
+    bf16 (14 heads: two per workgroup, direct-to-LDS K/V)."""
     import dataclasses
     dims = dataclasses.replace(synth.DIMS_TINY if base == "tiny" else synth.DIMS_06B, window_chunks=window_chunks)
     w = synth.make_weights(dims, 110 + window_chunks)
