@@ -496,6 +496,10 @@ def main():
         "tokens_per_s": round(T * args.steps / dt, 1),
         "mfma_util_pct": round(100.0 * total_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 2),
         "roofline": roof,
+        # the whole step against the time its algorithmic flops need at the bf16 peak
+        "step_roofline": {"algorithmic_tflop": round(total_flops / 1e12, 3),
+                          "nameplate_ms": round(total_flops / PEAK_BF16_TFLOPS / 1e9, 3),
+                          "frac_of_nameplate": round(total_flops / PEAK_BF16_TFLOPS / 1e9 / ms_step, 4)},
         "kernels": kernels,
         "kernels_note": f"per-kernel table from {prof_steps} separate steps with events around every launch; "
                         "the timed steps carry events only around the dominant kernel",
@@ -509,6 +513,8 @@ def main():
         meas = c["mfma_bf16_random_tflops"] if roof["unit"] == "TFLOP/s" else c["hbm_read_gbs"]
         roof["measured_ceiling"] = meas
         roof["frac_of_measured_ceiling"] = roof["achieved"] / meas
+        res["step_roofline"]["measured_ceiling_ms"] = round(total_flops / (meas_mfma := c["mfma_bf16_random_tflops"]) / 1e9, 3)
+        res["step_roofline"]["frac_of_measured"] = round(total_flops / meas_mfma / 1e9 / ms_step, 4)
         for ent in kernels.values():
             if "frac_of_bf16_peak" in ent:
                 ent["frac_of_measured_mfma"] = round(ent["tflops"] / c["mfma_bf16_random_tflops"], 4)
