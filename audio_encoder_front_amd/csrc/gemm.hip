@@ -20,8 +20,12 @@
 // (l%8) ^ (row%8) of its row, an XOR swizzle that makes the 16-byte fragment
 // reads of 8 consecutive rows hit 8 different 16-byte bank groups.  Chunks
 // outside the matrix (ragged M/N/K, conv padding) read as zeros.  While
-// stage k is multiplied, the weights of stage k+1 and the A rows of stage
-// k+2 are in flight: a ring of three A stages and two weight stages.
+// stage k is multiplied, stage k+1 of one operand and stage k+2 of the other
+// are in flight: a ring of three stages for the operand that runs two ahead
+// and two for the other.  The conv and gather loaders run A two ahead (their
+// input streams from HBM); the dense loader runs the weights two ahead.  With
+// dense activations every concurrent tile of an XCD asks for the same weight
+// slice at the same moment, so one L2 miss stalls up to eight workgroups.
 //
 // The MFMA is issued transposed (weights as the A operand): lane l then holds
 // 4 consecutive output columns of one output row.  After the K loop the tile
@@ -47,6 +51,7 @@ __device__ __align__(16) uint4 g_zero16[2];
 template <typename T>
 struct DenseA {
     static constexpr bool kBuffer = true;
+    static constexpr bool kWeightsAhead = true;     // weights two stages ahead, A one
     const T* a;
     int M, K, lda;
     template <int AI, int RS>
@@ -69,6 +74,7 @@ struct DenseA {
 template <typename T>
 struct GatherA {   // row m of the GEMM is row src[m] of a
     static constexpr bool kBuffer = false;
+    static constexpr bool kWeightsAhead = false;
     const T* a;
     const int* src;
     int M, K;
@@ -94,6 +100,7 @@ struct GatherA {   // row m of the GEMM is row src[m] of a
 template <typename T>
 struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
     static constexpr bool kBuffer = true;
+    static constexpr bool kWeightsAhead = false;
     const T* in;
     int M, Hin, Win, C, Hout, Wout;
     bool time_major;                  // output row order (chunk, j, i) instead of (chunk, i, j)
@@ -347,9 +354,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     constexpr int STAGE = ASTAGE + BSTAGE;
     static_assert(BM % (RPD * NW) == 0 && BN % (RPD * NW) == 0, "tile/waves mismatch");
     static_assert(TN >= 3, "the two-ahead weight prefetch needs at least 3 weight tiles");
-    // Three stages of A (a ring: its loads run two stages ahead), then two of
-    // the weights (one stage ahead): 160 KB for the 256 x 256 tile.
-    __shared__ __align__(1024) char smem[3 * ASTAGE + 2 * BSTAGE];
+    // The operand that runs two stages ahead has a ring of three LDS stages,
+    // the other two: 160 KB for the 256 x 256 tile.  Rings: A at the start of
+    // the LDS, the weights after it.
+    constexpr bool WA = AL::kWeightsAhead;
+    constexpr int ARING = WA ? 2 : 3, BRING = WA ? 3 : 2;
+    __shared__ __align__(1024) char smem[ARING * ASTAGE + BRING * BSTAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     };
     auto issue_b = [&](int kt, int buf) {
         const auto kw = wl.kprep(kt * KSTEP + kc * PER);
-        const unsigned sb = lds0 + 3 * ASTAGE + buf * BSTAGE + wave_u * (BI * 1024);
+        const unsigned sb = lds0 + ARING * ASTAGE + buf * BSTAGE + wave_u * (BI * 1024);
 #pragma unroll
         for (int q = 0; q < BI; ++q) dma16_buf(rw, wl.boff(wlane, q, kw), sb + q * 1024);
     };
@@ -406,9 +416,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
     const int kper = (nk_all + (int)gridDim.y - 1) / (int)gridDim.y;
     const int kt0 = (int)blockIdx.y * kper;
     const int nk = max(0, min(nk_all, kt0 + kper) - kt0);
-    issue_a(kt0, 0);
-    issue_b(kt0, 0);
-    issue_a(kt0 + 1, 1);
+    if constexpr (WA) {
+        issue_b(kt0, 0);
+        issue_a(kt0, 0);
+        issue_b(kt0 + 1, 1);
+    } else {
+        issue_a(kt0, 0);
+        issue_b(kt0, 0);
+        issue_a(kt0 + 1, 1);
+    }
     const int fr = lane & 15, fg = lane >> 4;
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -433,17 +449,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
         // into the idle buffer, past the last of a split they fetch the next
         // split's first stage unused), kept in this basic block so that the
         // scheduling below can spread them between the MFMA groups.
-        // The A loads run two stages ahead (the activations and the conv
-        // input come from HBM more often than the L2-resident weights), issued
-        // after the weights' one-ahead loads so that the wait at the end of
-        // the iteration can leave them in flight: vector-memory loads complete
-        // in issue order.
+        // The two-ahead loads are issued after the one-ahead ones so that the
+        // wait at the end of the iteration can leave them in flight:
+        // vector-memory loads complete in issue order.
         const int kt = kt0 + i;
-        const int abuf = i % 3;
-        issue_b(kt + 1, (i + 1) & 1);
-        issue_a(kt + 2, abuf == 0 ? 2 : abuf - 1);
+        const int r3 = i % 3, r3n = r3 == 0 ? 2 : r3 - 1;   // slots i and i + 2 of a three-stage ring
+        const int abuf = WA ? (i & 1) : r3, bbuf = WA ? r3 : (i & 1);
+        if constexpr (WA) {
+            issue_a(kt + 1, (i + 1) & 1);
+            issue_b(kt + 2, r3n);
+        } else {
+            issue_b(kt + 1, (i + 1) & 1);
+            issue_a(kt + 2, r3n);
+        }
         const char* a = smem + abuf * ASTAGE + (wm * TM * 16 + fr) * BKB;
-        const char* bp = smem + 3 * ASTAGE + (i & 1) * BSTAGE + (wn * TN * 16 + fr) * BKB;
+        const char* bp = smem + ARING * ASTAGE + bbuf * BSTAGE + (wn * TN * 16 + fr) * BKB;
         // Fragments: the TM activation fragments of a 64-byte K block stay in
         // registers while the TN weight fragments stream through a two-ahead
         // prefetch; the next K block's activation fragments are fetched during
@@ -489,11 +509,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(AL al, const T* __re
                 __builtin_amdgcn_sched_group_barrier(0x008, TM * MPK, 0);
             }
         }
-        // everything but this iteration's AI A loads: stage i + 1 has landed
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AI) : "memory");
+        // everything but this iteration's two-ahead loads: stage i + 1 has landed
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WA ? BI : AI) : "memory");
         __syncthreads();
     }
-    // the last A loads (zeros or an unused stage) land before the epilogue
+    // the last two-ahead loads (zeros or an unused stage) land before the epilogue
     // reuses the LDS
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
