@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqa_encoder.so")
-SOURCES = ["frontend.hip", "stem.hip", "gemm.hip", "norm_attn.hip", "resample.hip", "thinker.hip", "encoder.cpp",
+SOURCES = ["frontend.hip", "stem.hip", "stem_fused.hip", "gemm.hip", "norm_attn.hip", "resample.hip", "thinker.hip", "encoder.cpp",
            "thinker_host.cpp"]
 # the ceiling probes the benchmark runs beside the encoder (not the encoder's path)
 PROBE_SOURCES = ["probe.hip"]

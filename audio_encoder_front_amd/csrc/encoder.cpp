@@ -400,7 +400,7 @@ QA_API qa_encoder* qa_encoder_create(const qa_weights* w, const qa_dims* d) {
             for (int k = 0; k < 9; ++k) r[(size_t)k * C + c] = v[(size_t)c * 9 + k];
         e->conv1_w = put_f32(r);
         e->conv1_b = put_f32(f32vec(w->conv1_b, C));
-        if (d->dtype == QA_DTYPE_BF16 && C <= qa::kConv1MfmaMaxC) {
+        if (d->dtype == QA_DTYPE_BF16 && C <= qa::kStemFusedMaxC) {
             // A operand of lane l for channel tile t: channel 32 (t / 2) + 8 (r / 4) +
             // 4 (t % 2) + r % 4 with r = l % 16, K entries k = 8 (l / 16) + e: tap
             // k / 3 for k < 27 (three copies, one per input part), the bias at
@@ -650,7 +650,10 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     const size_t o_logmel = slot((size_t)n_frames * qa::kMels * 4);
     const size_t o_key = slot((size_t)n_clips * 4);
     const size_t o_flag = slot(4);
-    const size_t o_c1 = slot((size_t)n_chunks * 64 * 50 * C * sizeof(T));
+    // bf16 with the MFMA conv1: conv1 and conv2 run as one kernel and conv1's
+    // output is never stored
+    const bool fused_stem = std::is_same<T, qa::bf16>::value && e->conv1_frag != 0;
+    const size_t o_c1 = slot(fused_stem ? 0 : (size_t)n_chunks * 64 * 50 * C * sizeof(T));
     const size_t o_c2 = slot((size_t)n_chunks * 32 * 25 * C * sizeof(T));
     const size_t o_c3 = slot((size_t)n_chunks * 13 * 16 * C * sizeof(T));
     const size_t o_x = slot((size_t)n_tok * D * 4);
@@ -765,16 +768,17 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
                                        e->W<int>(e->melb0), logmel, key, flag));
     QA_LAUNCH("normalize", qa::normalize(s, logmel, d_clips, d_tiles, n_tiles, key));
     if constexpr (std::is_same<T, qa::bf16>::value) {
-        if (e->conv1_frag)
-            QA_LAUNCH("conv1", qa::conv1_mfma(s, logmel, d_chunks, n_chunks, e->W<uint4>(e->conv1_frag), C, c1));
+        if (fused_stem)
+            QA_LAUNCH("stem12", qa::stem12(s, logmel, d_chunks, n_chunks, e->W<uint4>(e->conv1_frag), e->W<T>(e->conv2_w),
+                                           e->W<float>(e->conv2_b), C, c2));
         else
             QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
     } else {
         QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
     }
-    const bool c1_blocked = std::is_same<T, qa::bf16>::value && e->conv1_frag != 0;   // MFMA conv1 layout
-    QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1, n_chunks, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b), c2, false, c1_blocked));
-    QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2, n_chunks, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b), c3, true, false));
+    if (!fused_stem)   // NHWC conv1 output (VALU conv1)
+        QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1, n_chunks, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b), c2, false));
+    QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2, n_chunks, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b), c3, true));
     QA_LAUNCH("conv_out", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), x, nullptr,
                                           part, part_elems));
     if (taps)

@@ -104,9 +104,7 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
     const T* in;
     int M, Hin, Win, C, Hout, Wout;
     bool time_major;                  // output row order (chunk, j, i) instead of (chunk, i, j)
-    // Input layout per chunk: NHWC [Hin][Win][C] (pstride = C, cbstride = 32) or
-    // channel-blocked [C / 32][Hin][Win][32] (pstride = 32, cbstride = Hin Win 32).
-    int pstride, cbstride;
+    // input layout per chunk: NHWC [Hin][Win][C]
     // A tile of up to 256 output rows touches at most 3 chunks, so offsets from
     // the tile's first chunk stay far below 4 GB.
     template <int AI, int RS>
@@ -141,7 +139,7 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
         const int cb = k0 / (9 * kConvCB), rem = k0 - cb * (9 * kConvCB);
         const int tap = rem / kConvCB, ci = cb * kConvCB + (rem - tap * kConvCB);
         const int a = tap / 3;
-        return KCtx{a, tap - 3 * a, (unsigned)((cb * cbstride + (ci - cb * kConvCB)) * (int)sizeof(T)), k0 < 9 * C};
+        return KCtx{a, tap - 3 * a, (unsigned)(ci * (int)sizeof(T)), k0 < 9 * C};
     }
     template <int AI, int RS>
     __device__ unsigned boff(const Lane<AI, RS>& l, int q, const KCtx& k) const {
@@ -149,7 +147,7 @@ struct ConvA {     // implicit im2col of a 3x3 stride-2 pad-1 conv
         const int col = (int)(short)(l.rc[q] & 0xffff) + k.b;
         if (l.cofs[q] < 0 || !k.ok || (unsigned)r >= (unsigned)Hin || (unsigned)col >= (unsigned)Win)
             return kOobOffset;
-        return (unsigned)((l.cofs[q] + (r * Win + col) * pstride) * (int)sizeof(T)) + k.off;
+        return (unsigned)((l.cofs[q] + (r * Win + col) * C) * (int)sizeof(T)) + k.off;
     }
 };
 
@@ -604,12 +602,11 @@ static hipError_t run(hipStream_t s, const AL& al, int M, const T* w, int N, int
 
 template <typename T>
 hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win, int C,
-                     const T* w, const float* bias, T* out, bool time_major, bool blocked_in) {
+                     const T* w, const float* bias, T* out, bool time_major) {
     const int Hout = (Hin + 1) / 2, Wout = (Win + 1) / 2;
     const int M = n_chunks * Hout * Wout;
     if (C % kConvCB) return hipErrorInvalidValue;
-    ConvA<T> al{in, M, Hin, Win, C, Hout, Wout, time_major, blocked_in ? kConvCB : C,
-                blocked_in ? Hin * Win * kConvCB : kConvCB};
+    ConvA<T> al{in, M, Hin, Win, C, Hout, Wout, time_major};
     EpiBias<T, true> ep{out, bias, M, C};
     if (C % Elem<T>::per16) return hipErrorInvalidValue;
     return time_major ? run<kConv3>(s, al, M, w, C, 9 * C, ep) : run<kConv2>(s, al, M, w, C, 9 * C, ep);
@@ -760,7 +757,7 @@ hipError_t thinker_logits(hipStream_t s, const T* a, const int* rows, int n_rows
 
 #define QA_INST(T)                                                                                    \
     template hipError_t conv3x3s2<T>(hipStream_t, const T*, int, int, int, int, const T*, const float*, \
-                                     T*, bool, bool);                                                 \
+                                     T*, bool);                                                       \
     template hipError_t conv_out<T>(hipStream_t, const T*, const int*, int, int, const T*, int,        \
                                     const float*, float*, float*, float*, size_t);                                    \
     template hipError_t gemm_bias<T>(hipStream_t, const T*, int, int, const T*, int, const float*, T*, \

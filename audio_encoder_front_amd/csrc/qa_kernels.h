@@ -66,19 +66,21 @@ hipError_t normalize(hipStream_t s, float* logmel, const ClipInfo* clips, const 
 template <typename T>
 hipError_t conv1(hipStream_t s, const float* logmel, const ChunkInfo* chunks, int n_chunks,
                  const float* w9c, const float* bias, int C, T* out);
-// bf16 mode, C a multiple of 32 and at most 512: the same conv1 on MFMA, with
-// pre-laid-out weight fragments wfrag[C / 16][64][8] (bias in K slot 27);
-// output channel-blocked [n_chunks][C/32][64][50][32].
-constexpr int kConv1MfmaMaxC = 512;
-hipError_t conv1_mfma(hipStream_t s, const float* logmel, const ChunkInfo* chunks, int n_chunks,
-                      const uint4* wfrag, int C, bf16* out);
-// conv 3x3 stride 2 pad 1 as an implicit GEMM over input [n_chunks][Hin][Win][C]
-// (NHWC) or, with blocked_in, [n_chunks][C/32][Hin][Win][32]; weights [C_out][9*C]
+// conv1 and conv2 in one kernel (bf16, C a multiple of 32 and at most 512):
+// conv2's output NHWC [n_chunks][32][25][C] from the normalised log-mel, with
+// conv1 as bf16 MFMA fragments wfrag[C / 16][64][8] (3-way split input, bias in
+// K slot 27) and conv2's weights w2 [C][9C] (K order as conv3x3s2) and bias b2;
+// conv1's output is never stored.
+constexpr int kStemFusedMaxC = 512;
+hipError_t stem12(hipStream_t s, const float* logmel, const ChunkInfo* chunks, int n_chunks, const uint4* wfrag,
+                  const bf16* w2, const float* b2, int C, bf16* out);
+// conv 3x3 stride 2 pad 1 as an implicit GEMM over NHWC input [n_chunks][Hin][Win][C];
+// weights [C_out][9*C]
 // with k = (ci/32)*288 + (a*3+b)*32 + ci%32.  Output is NHWC
 // [n_chunks][Hout][Wout][C] (time_major=false) or [n_chunks][Wout][Hout][C].
 template <typename T>
 hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win, int C,
-                     const T* w, const float* bias, T* out, bool time_major, bool blocked_in);
+                     const T* w, const float* bias, T* out, bool time_major);
 // x[t][:] = A[src[t]][:] . Wout^T + pe[src[t] % 13][:]  (fp32), and optionally
 // tap[t][:] without the PE.
 // part (part_elems floats, may be null): workspace for split-K, used when

@@ -1,0 +1,254 @@
+// conv1 -> conv2 of the conv stem in one kernel (bf16 encoders): conv2's
+// implicit GEMM takes its A operand from a conv1 patch that the workgroup
+// computes into LDS, one 32-channel slab at a time, so conv1's output (two
+// bytes per channel and pixel, 3.7 GB for 20 minutes of audio) never goes to
+// HBM (qwenasr.cpp ARCHITECTURE.md "Conv2d subsampling stem": conv2d k3 s2 p1
+// 1 -> C, GELU, conv2d k3 s2 p1 C -> C, GELU, per 100-frame chunk; OneSpeech
+// "Front end and graph numerics": chunks padded independently).
+//
+// Tile: one chunk, 5 of conv2's 25 time columns x all 32 frequency rows (160
+// output pixels, row order (column, row) inside the tile) x 256 output
+// channels; 8 waves, each with all 160 pixels x 32 channels.  The K order is
+// conv2's (32-channel slab, tap, channel), so every 32-wide MFMA K block is one
+// (slab, tap).  Per slab the MFMAs read a conv1 patch from LDS: conv1's outputs
+// of the tile's receptive field for the slab's 32 channels (11 conv1 columns x
+// 65 conv1 rows, -1 .. 63; row -1 and column -1 are conv2's zero padding),
+// computed by a split-input MFMA (below) and the GELU.  The
+// patch is double-buffered: while the waves multiply slab s they compute slab
+// s + 1's patch into the other buffer (one barrier per slab).  A wave's 32
+// weight rows are its own, so they go global -> registers, three taps ahead,
+// with no LDS and no barrier.
+//
+// conv1 on MFMA: K = 9 taps x 3 bf16 parts (hi + mid + lo, which add up to
+// the fp32 log-mel value to within one fp32 ulp) + 1 bias slot = 28 <= 32, so
+// one v_mfma_f32_16x16x32_bf16 gives 16 channels x 16 pixels of conv1 in fp32;
+// the fragments' channel order (see the weight packing) gives each lane 8
+// consecutive channels of one pixel from two MFMAs, one 16-byte patch store.
+// conv2's accumulators take the (slab, tap) blocks in K order, as gemm_kernel
+// with ConvA does over a stored conv1 output (the path of fp32 and of stems
+// wider than 512 channels), and the output was checked bit-identical to that
+// route when both existed.
+//
+// LDS: two patches (46,464 B each) and the tile's log-mel window (11,868 B).
+// Patch layout: [conv1 column 11][row parity 2][row / 2 33][32 channels]: a
+// conv2 tap reads the conv1 rows 2 i + a of 16 consecutive output rows i,
+// which this layout keeps 64 bytes apart; the 16-byte channel chunks are
+// XOR-swizzled by (row / 2) / 2 so that the reads of 8 consecutive rows hit 8
+// different bank groups.  Slot (parity 1, row / 2 = 32) of column 0 is never
+// read: pixel groups past the patch write their results there.
+#include <type_traits>
+
+#include "qa_device.h"
+#include "qa_kernels.h"
+
+namespace qa {
+
+constexpr int kFsCols = 5;                              // conv2 time columns per tile
+constexpr int kFsTilesPerChunk = 25 / kFsCols;          // 5
+constexpr int kFsM = kFsCols * 32;                      // 160 output pixels
+constexpr int kFsPcol = 2 * kFsCols + 1;                // 11 conv1 columns
+constexpr int kFsProw = 65;                             // conv1 rows -1 .. 63
+constexpr int kFsRi = 33;                               // patch rows per parity
+constexpr int kFsPix = kFsPcol * kFsProw;               // 715 patch pixels
+constexpr int kFsGroups = (kFsPix + 15) / 16;           // 45 MFMA pixel groups
+constexpr int kFsGpw = (kFsGroups + 7) / 8;             // pixel groups per wave (6)
+constexpr int kFsPatchBytes = kFsPcol * 2 * kFsRi * 64; // 46,464
+constexpr int kFsMelRows = kMels + 1;                   // mel rows -1 .. 127
+constexpr int kFsMelT = 4 * kFsCols + 3;                // 23 frames
+constexpr int kFsMelBytes = kFsMelRows * kFsMelT * 4;   // 11,868
+constexpr int kFsOffMel = 2 * kFsPatchBytes;
+constexpr int kFsLds = kFsOffMel + kFsMelBytes;         // 104,796 B
+constexpr int kFsWAhead = 3;                            // weight taps in flight per wave
+static_assert(kFsM * 256 * 2 <= 2 * kFsPatchBytes, "epilogue staging fits the patches");
+static_assert(9 % kFsWAhead == 0, "the weight ring position of a tap is the same in every slab");
+
+__device__ __forceinline__ int fs_patch_off(int pcol, int prow, int chunk) {
+    const int par = prow & 1, ri = prow >> 1;
+    return ((pcol * 2 + par) * kFsRi + ri) * 64 + ((chunk ^ ((ri >> 1) & 3)) << 4);
+}
+constexpr int kFsDummy = (1 * kFsRi + 32) * 64;         // column 0, parity 1, row / 2 32: never read
+
+template <int NCB>   // 32-channel slabs of conv1's output = conv2's input (C = 32 NCB)
+__global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ logmel,
+                                                     const ChunkInfo* __restrict__ chunks,
+                                                     const uint4* __restrict__ wfrag,
+                                                     const bf16* __restrict__ w2,
+                                                     const float* __restrict__ b2,
+                                                     bf16* __restrict__ out) {
+    constexpr int C = 32 * NCB, K = 9 * C, NT = 9 * NCB;   // NT: (slab, tap) K blocks
+    __shared__ __align__(1024) char smem[kFsLds];
+    float* img = reinterpret_cast<float*>(smem + kFsOffMel);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fr = lane & 15, fg = lane >> 4;
+    const int chunk = blockIdx.x / kFsTilesPerChunk, j0 = (blockIdx.x % kFsTilesPerChunk) * kFsCols;
+    const int n0 = blockIdx.y * 256 + wave * 32;          // this wave's first output channel
+    const ChunkInfo ci = chunks[chunk];
+
+    // ---- this wave's weight rows n0 + 16 j + fr (rows past C repeat row C - 1:
+    // their outputs are never stored); K block t = (slab, tap) at element 32 t
+    const bf16* wrow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wrow[j] = w2 + (size_t)min(n0 + 16 * j + fr, C - 1) * K + 8 * fg;
+    uint4 wb[kFsWAhead][2];
+    auto load_w = [&](int t, uint4* dst) {
+        const int tc = min(t, NT - 1);                   // past the last block: a repeat, unused
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dst[j] = ld16(wrow[j] + 32 * tc);
+    };
+#pragma unroll
+    for (int r = 0; r < kFsWAhead; ++r) load_w(r, wb[r]);
+
+    // ---- the tile's log-mel window: rows -1 .. 127, frames 4 j0 - 3 .. 4 j0 + 19
+    // (zeros outside the chunk's frames), [frame][row]
+    for (int idx = tid; idx < kFsMelRows * kFsMelT; idx += 512) {
+        const int t = idx / kFsMelRows, rr = idx - t * kFsMelRows;
+        const int f = rr - 1, tt = 4 * j0 - 3 + t;
+        float v = 0.f;
+        if (f >= 0 && tt >= 0 && tt < ci.m) v = logmel[(size_t)(ci.frame_row0 + tt) * kMels + f];
+        img[idx] = v;
+    }
+
+    // ---- accumulators, bias as the start value: lane holds out[m = fr][n = 4 fg + r]
+    f32x4 acc[10][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = n0 + j * 16 + 4 * fg;
+        f32x4 b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[r] = n + r < C ? b2[n + r] : 0.f;
+#pragma unroll
+        for (int f = 0; f < 10; ++f) acc[f][j] = b;
+    }
+    __syncthreads();                                     // the mel window is in LDS
+
+    // ---- conv1 B operands of this wave's pixel groups (the same for every
+    // slab): lane (px, g) holds K entries 8 g .. 8 g + 7 of pixel px: tap k / 3
+    // (dy = tap / 3, dx = tap % 3), part k % 3 of the 3-way bf16 split, k = 27
+    // the constant 1 of the bias slot.  Each group's LDS destination in the
+    // patch (the dummy slot for pixels past it) and its padding flag.
+    uint4 bop[kFsGpw];
+    int pdst[kFsGpw];
+    bool ppad[kFsGpw];
+#pragma unroll
+    for (int u = 0; u < kFsGpw; ++u) {
+        const int p = (wave + 8 * u) * 16 + fr;
+        const bool in = p < kFsPix;
+        const int pc = in ? p / kFsProw : 0, pr = in ? p - pc * kFsProw : 1;
+        pdst[u] = in ? fs_patch_off(pc, pr, fg) : kFsDummy + (fg << 4);
+        ppad[u] = pr == 0 || (pc == 0 && j0 == 0);
+        const int base = 2 * pc * kFsMelRows + 2 * max(pr, 1) - 2;   // rows past the top are padding
+        bf16 bv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = 8 * fg + e;
+            const int tap = k / 3, q = k - 3 * tap;
+            const float x = k < 27 ? img[base + (tap % 3) * kFsMelRows + tap / 3] : 0.f;
+            const bf16 hi = (bf16)x;
+            const float r1 = x - (float)hi;
+            const bf16 mid = (bf16)r1;
+            const bf16 lo = (bf16)(r1 - (float)mid);
+            bv[e] = k < 27 ? (q == 0 ? hi : q == 1 ? mid : lo) : (k == 27 ? (bf16)1.0f : (bf16)0.0f);
+        }
+        const bf16x8 b8 = {bv[0], bv[1], bv[2], bv[3], bv[4], bv[5], bv[6], bv[7]};
+        bop[u] = __builtin_bit_cast(uint4, b8);
+    }
+    // one pixel group of slab s's patch into buffer pb
+    auto conv1_group = [&](int u, const uint4& wa0, const uint4& wa1, char* pb) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa0),
+                                                                 __builtin_bit_cast(bf16x8, bop[u]), z, 0, 0, 0);
+        const f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa1),
+                                                                 __builtin_bit_cast(bf16x8, bop[u]), z, 0, 0, 0);
+        const bf16x8 o = {(bf16)gelu_erf_bf16(a0[0]), (bf16)gelu_erf_bf16(a0[1]), (bf16)gelu_erf_bf16(a0[2]),
+                          (bf16)gelu_erf_bf16(a0[3]), (bf16)gelu_erf_bf16(a1[0]), (bf16)gelu_erf_bf16(a1[1]),
+                          (bf16)gelu_erf_bf16(a1[2]), (bf16)gelu_erf_bf16(a1[3])};
+        *reinterpret_cast<uint4*>(pb + pdst[u]) = ppad[u] ? make_uint4(0u, 0u, 0u, 0u) : __builtin_bit_cast(uint4, o);
+    };
+    {
+        const uint4 wa0 = wfrag[lane], wa1 = wfrag[64 + lane];
+#pragma unroll
+        for (int u = 0; u < kFsGpw; ++u) conv1_group(u, wa0, wa1, smem);
+    }
+    __syncthreads();                                     // slab 0's patch
+
+    // one slab: 9 taps of 20 MFMAs from patch buffer s & 1; with NEXT, slab
+    // s + 1's patch into the other buffer, one pixel group every 1.5 taps
+    auto slab = [&](int s, auto next_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const char* pa = smem + (s & 1) * kFsPatchBytes;
+        char* pn = smem + ((s + 1) & 1) * kFsPatchBytes;
+        uint4 wa0, wa1;
+        if constexpr (NEXT) {
+            wa0 = wfrag[(size_t)(2 * s + 2) * 64 + lane];
+            wa1 = wfrag[(size_t)(2 * s + 3) * 64 + lane];
+        }
+#pragma unroll
+        for (int tap = 0; tap < 9; ++tap) {
+            const int a = tap / 3, bb = tap - 3 * a;
+            const uint4 fb0 = wb[tap % kFsWAhead][0], fb1 = wb[tap % kFsWAhead][1];
+            load_w(9 * s + tap + kFsWAhead, wb[tap % kFsWAhead]);
+            uint4 fa[10];
+#pragma unroll
+            for (int f = 0; f < 10; ++f) {
+                const int jj = f >> 1, i = (f & 1) * 16 + fr;
+                fa[f] = ld16(pa + fs_patch_off(2 * jj + bb, 2 * i + a, fg));
+            }
+#pragma unroll
+            for (int f = 0; f < 10; ++f) mfma_kblock(bf16(), fb0, fa[f], acc[f][0]);
+#pragma unroll
+            for (int f = 0; f < 10; ++f) mfma_kblock(bf16(), fb1, fa[f], acc[f][1]);
+            if constexpr (NEXT) {
+                if (tap % 3 != 2) conv1_group(2 * (tap / 3) + tap % 3, wa0, wa1, pn);
+            }
+        }
+        __syncthreads();   // reads of buffer s & 1 done; slab s + 1's patch complete
+    };
+    for (int s = 0; s + 1 < NCB; ++s) slab(s, std::true_type{});
+    slab(NCB - 1, std::false_type{});
+
+    // ---- epilogue: GELU, bf16, staged row-major through the patch buffers
+    // (rows of 512 B, 16-byte chunks XOR-swizzled by row % 16), then whole
+    // 16-byte chunks of output rows: pixel (column jj, row i) of the tile is
+    // row (chunk, i, j0 + jj) of conv2's NHWC output
+#pragma unroll
+    for (int f = 0; f < 10; ++f) {
+        const int m = f * 16 + fr;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = wave * 32 + j * 16 + 4 * fg;  // 4 channels = half of chunk n / 8
+            const int c16 = (n >> 3) ^ (m & 15);
+            store4(reinterpret_cast<bf16*>(smem + m * 512 + (c16 << 4) + ((n & 4) << 1)),
+                   gelu_erf_bf16(acc[f][j][0]), gelu_erf_bf16(acc[f][j][1]), gelu_erf_bf16(acc[f][j][2]),
+                   gelu_erf_bf16(acc[f][j][3]));
+        }
+    }
+    __syncthreads();
+    bf16* obase = out + (size_t)chunk * 800 * C;
+    const int nt0 = blockIdx.y * 256;
+    for (int idx = tid; idx < kFsM * 32; idx += 512) {
+        const int m = idx >> 5, c = idx & 31;
+        const int n = nt0 + 8 * c;
+        if (n >= C) continue;
+        const int jj = m >> 5, i = m & 31;
+        const uint4 v = ld16(smem + m * 512 + ((c ^ (m & 15)) << 4));
+        *reinterpret_cast<uint4*>(obase + ((size_t)i * 25 + j0 + jj) * C + n) = v;
+    }
+}
+
+hipError_t stem12(hipStream_t s, const float* logmel, const ChunkInfo* chunks, int n_chunks, const uint4* wfrag,
+                  const bf16* w2, const float* b2, int C, bf16* out) {
+    if (n_chunks <= 0) return hipSuccess;
+    const dim3 grid((unsigned)(n_chunks * kFsTilesPerChunk), (unsigned)((C + 255) / 256));
+    switch (C) {   // C is a multiple of 32, at most 512 (the MFMA conv1's limit)
+#define QA_S12(ncb) case 32 * ncb: stem12_kernel<ncb><<<grid, 512, 0, s>>>(logmel, chunks, wfrag, w2, b2, out); break;
+        QA_S12(1) QA_S12(2) QA_S12(3) QA_S12(4) QA_S12(5) QA_S12(6) QA_S12(7) QA_S12(8)
+        QA_S12(9) QA_S12(10) QA_S12(11) QA_S12(12) QA_S12(13) QA_S12(14) QA_S12(15) QA_S12(16)
+#undef QA_S12
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qa

@@ -69,6 +69,10 @@ def kernel_work(d, lengths):
     fr_all = fr + sum(1 for n in lengths if n)
     work = {
         "frontend": (fr_all * FRONT_BF16_EXEC_FLOPS, sum(lengths) * 4 + fr * 128 * 4, "bf16"),
+        # conv1 + conv2 in one kernel (bf16 stems up to 512 channels): the
+        # method's conv1 and conv2 flops; log-mel in, conv2's output and weights
+        "stem12": (2 * ch * 64 * 50 * C * 9 + 2 * ch * 800 * C * 9 * C,
+                   fr * 128 * 4 + ch * 800 * C * e + 9 * C * C * e, "bf16"),
         "conv2": (2 * ch * 800 * C * 9 * C, ch * 64 * 50 * C * e + ch * 800 * C * e + 9 * C * C * e, "bf16"),
         "conv3": (2 * ch * 208 * C * 9 * C, ch * 800 * C * e + ch * 208 * C * e + 9 * C * C * e, "bf16"),
         "conv_out": (2 * T * 16 * C * D, T * 16 * C * e + 16 * C * D * e + T * D * 4, "bf16"),
@@ -89,7 +93,7 @@ def kernel_work(d, lengths):
 # Source files whose kernels the HBM-traffic figure in profiles/ was taken on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "b17_20m_traffic.json")
 KERNEL_SOURCES = ["audio_encoder_front_amd/csrc/" + f for f in
-                  ("gemm.hip", "stem.hip", "frontend.hip", "norm_attn.hip", "encoder.cpp", "qa_device.h",
+                  ("gemm.hip", "stem.hip", "stem_fused.hip", "frontend.hip", "norm_attn.hip", "encoder.cpp", "qa_device.h",
                    "qa_kernels.h")]
 
 

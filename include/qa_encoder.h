@@ -170,8 +170,10 @@ int qa_encode(qa_encoder *e, const float *pcm, const int64_t *lengths, int n_cli
  * device, pinned-host or event allocation: the small planning tables go to
  * the device from pageable host memory.  A batch whose workspace exceeds the
  * array is refused with INVALID_PARAMS before any device work (a 30 s clip of
- * the 0.6B shape needs about 136 MiB; the workspace grows with the total
- * audio: roughly 4.6 MiB per second at 480 stem channels).  Taps and
+ * the 0.6B bf16 shape needs about 47 MiB; the workspace grows with the total
+ * audio: roughly 1.2 MiB per second at 480 stem channels, about 3.5 times
+ * that for fp32 encoders and stems wider than 512 channels, which store
+ * conv1's output).  Taps and
  * profiling events are not recorded by this call (qa_encoder_tap then fails
  * until the next qa_encode with taps).  Every call on one GPU, through any
  * handle, shares that GPU's array and overwrites it: calls that overlap on

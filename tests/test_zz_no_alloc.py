@@ -50,7 +50,7 @@ def test_noalloc_refuses_batches_beyond_the_scratch():
     import audio_encoder_front_amd as qa
     wl = synth.WORKLOADS["b06_1"]
     enc = make_encoder(wl.dims, synth.make_weights(wl.dims, wl.weight_seed))
-    lens = [480000] * 3                      # three 30 s clips: about 400 MiB of workspace
+    lens = [480000] * 8                      # eight 30 s clips: about 320 MiB of workspace
     pcm = torch.zeros(sum(lens), device="cuda")
     out = torch.empty((sum(qa.qa_encode_num_tokens(n) for n in lens), wl.dims.output_dim), device="cuda")
     with pytest.raises(qa.QAError) as ei:
