@@ -29,7 +29,10 @@
 // wider than 512 channels), and the output was checked bit-identical to that
 // route when both existed.
 //
-// LDS: two patches (46,464 B each) and the tile's log-mel window (11,868 B).
+// LDS: two patches (46,464 B each), the tile's log-mel window (11,868 B) and
+// the conv1 B operands of every wave's pixel groups (49,152 B; the same for
+// every slab, built once, kept out of the registers).  The first two
+// fragments of the next tap are read during the current tap's MFMAs.
 // Patch layout: [conv1 column 11][row parity 2][row / 2 33][32 channels]: a
 // conv2 tap reads the conv1 rows 2 i + a of 16 consecutive output rows i,
 // which this layout keeps 64 bytes apart; the 16-byte channel chunks are
@@ -57,7 +60,9 @@ constexpr int kFsMelRows = kMels + 1;                   // mel rows -1 .. 127
 constexpr int kFsMelT = 4 * kFsCols + 3;                // 23 frames
 constexpr int kFsMelBytes = kFsMelRows * kFsMelT * 4;   // 11,868
 constexpr int kFsOffMel = 2 * kFsPatchBytes;
-constexpr int kFsLds = kFsOffMel + kFsMelBytes;         // 104,796 B
+constexpr int kFsOffBop = (kFsOffMel + kFsMelBytes + 15) / 16 * 16;
+constexpr int kFsLds = kFsOffBop + 8 * kFsGpw * 64 * 16;   // + the conv1 B operands: 153,952 B
+constexpr int kFsPrefetch = 2;                          // fragments of the next tap read ahead
 constexpr int kFsWAhead = 3;                            // weight taps in flight per wave
 static_assert(kFsM * 256 * 2 <= 2 * kFsPatchBytes, "epilogue staging fits the patches");
 static_assert(9 % kFsWAhead == 0, "the weight ring position of a tap is the same in every slab");
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
     // (dy = tap / 3, dx = tap % 3), part k % 3 of the 3-way bf16 split, k = 27
     // the constant 1 of the bias slot.  Each group's LDS destination in the
     // patch (the dummy slot for pixels past it) and its padding flag.
-    uint4 bop[kFsGpw];
+    uint4* bop_lds = reinterpret_cast<uint4*>(smem + kFsOffBop) + wave * kFsGpw * 64 + lane;
     int pdst[kFsGpw];
     bool ppad[kFsGpw];
 #pragma unroll
@@ -152,15 +157,16 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
             bv[e] = k < 27 ? (q == 0 ? hi : q == 1 ? mid : lo) : (k == 27 ? (bf16)1.0f : (bf16)0.0f);
         }
         const bf16x8 b8 = {bv[0], bv[1], bv[2], bv[3], bv[4], bv[5], bv[6], bv[7]};
-        bop[u] = __builtin_bit_cast(uint4, b8);
+        bop_lds[u * 64] = __builtin_bit_cast(uint4, b8);
     }
     // one pixel group of slab s's patch into buffer pb
     auto conv1_group = [&](int u, const uint4& wa0, const uint4& wa1, char* pb) {
+        const uint4 bu = bop_lds[u * 64];
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa0),
-                                                                 __builtin_bit_cast(bf16x8, bop[u]), z, 0, 0, 0);
+                                                                 __builtin_bit_cast(bf16x8, bu), z, 0, 0, 0);
         const f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa1),
-                                                                 __builtin_bit_cast(bf16x8, bop[u]), z, 0, 0, 0);
+                                                                 __builtin_bit_cast(bf16x8, bu), z, 0, 0, 0);
         const bf16x8 o = {(bf16)gelu_erf_bf16(a0[0]), (bf16)gelu_erf_bf16(a0[1]), (bf16)gelu_erf_bf16(a0[2]),
                           (bf16)gelu_erf_bf16(a0[3]), (bf16)gelu_erf_bf16(a1[0]), (bf16)gelu_erf_bf16(a1[1]),
                           (bf16)gelu_erf_bf16(a1[2]), (bf16)gelu_erf_bf16(a1[3])};
@@ -184,16 +190,25 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
             wa0 = wfrag[(size_t)(2 * s + 2) * 64 + lane];
             wa1 = wfrag[(size_t)(2 * s + 3) * 64 + lane];
         }
+        auto read_frag = [&](int tap, int f) {
+            const int a = tap / 3, bb = tap - 3 * a, jj = f >> 1, i = (f & 1) * 16 + fr;
+            return ld16(pa + fs_patch_off(2 * jj + bb, 2 * i + a, fg));
+        };
+        uint4 fn[kFsPrefetch];
+#pragma unroll
+        for (int f = 0; f < kFsPrefetch; ++f) fn[f] = read_frag(0, f);
 #pragma unroll
         for (int tap = 0; tap < 9; ++tap) {
-            const int a = tap / 3, bb = tap - 3 * a;
             const uint4 fb0 = wb[tap % kFsWAhead][0], fb1 = wb[tap % kFsWAhead][1];
             load_w(9 * s + tap + kFsWAhead, wb[tap % kFsWAhead]);
             uint4 fa[10];
 #pragma unroll
-            for (int f = 0; f < 10; ++f) {
-                const int jj = f >> 1, i = (f & 1) * 16 + fr;
-                fa[f] = ld16(pa + fs_patch_off(2 * jj + bb, 2 * i + a, fg));
+            for (int f = 0; f < kFsPrefetch; ++f) fa[f] = fn[f];
+#pragma unroll
+            for (int f = kFsPrefetch; f < 10; ++f) fa[f] = read_frag(tap, f);
+            if (tap + 1 < 9) {
+#pragma unroll
+                for (int f = 0; f < kFsPrefetch; ++f) fn[f] = read_frag(tap + 1, f);
             }
 #pragma unroll
             for (int f = 0; f < 10; ++f) mfma_kblock(bf16(), fb0, fa[f], acc[f][0]);
