@@ -104,15 +104,26 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
     };
 #pragma unroll
     for (int r = 0; r < kFsWAhead; ++r) load_w(r, wb[r]);
+    const uint4 wa00 = wfrag[lane], wa01 = wfrag[64 + lane];   // conv1 fragments of slab 0
 
     // ---- the tile's log-mel window: rows -1 .. 127, frames 4 j0 - 3 .. 4 j0 + 19
     // (zeros outside the chunk's frames), [frame][row]
-    for (int idx = tid; idx < kFsMelRows * kFsMelT; idx += 512) {
-        const int t = idx / kFsMelRows, rr = idx - t * kFsMelRows;
-        const int f = rr - 1, tt = 4 * j0 - 3 + t;
-        float v = 0.f;
-        if (f >= 0 && tt >= 0 && tt < ci.m) v = logmel[(size_t)(ci.frame_row0 + tt) * kMels + f];
-        img[idx] = v;
+    // (all of a thread's loads are issued before its first store: one memory
+    // latency for the window, not one per element)
+    {
+        constexpr int NV = (kFsMelRows * kFsMelT + 511) / 512;
+        float v[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = tid + 512 * k;
+            const int t = idx / kFsMelRows, rr = idx - t * kFsMelRows;
+            const int f = rr - 1, tt = 4 * j0 - 3 + t;
+            const bool in = idx < kFsMelRows * kFsMelT && f >= 0 && tt >= 0 && tt < ci.m;
+            v[k] = in ? logmel[(size_t)(ci.frame_row0 + (in ? tt : 0)) * kMels + (in ? f : 0)] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (tid + 512 * k < kFsMelRows * kFsMelT) img[tid + 512 * k] = v[k];
     }
 
     // ---- accumulators, bias as the start value: lane holds out[m = fr][n = 4 fg + r]
@@ -172,11 +183,8 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
                           (bf16)gelu_erf_bf16(a1[2]), (bf16)gelu_erf_bf16(a1[3])};
         *reinterpret_cast<uint4*>(pb + pdst[u]) = ppad[u] ? make_uint4(0u, 0u, 0u, 0u) : __builtin_bit_cast(uint4, o);
     };
-    {
-        const uint4 wa0 = wfrag[lane], wa1 = wfrag[64 + lane];
 #pragma unroll
-        for (int u = 0; u < kFsGpw; ++u) conv1_group(u, wa0, wa1, smem);
-    }
+    for (int u = 0; u < kFsGpw; ++u) conv1_group(u, wa00, wa01, smem);
     __syncthreads();                                     // slab 0's patch
 
     // one slab: 9 taps of 20 MFMAs from patch buffer s & 1; with NEXT, slab
