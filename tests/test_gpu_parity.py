@@ -254,8 +254,8 @@ def test_other_window_sizes(base, window_chunks):
 
 def test_bf16_wide_stem_valu_conv1():
     """bf16 with 544 stem channels (> 512): conv1 takes the VALU kernel with an
-    NHWC output and conv2 gathers NHWC input instead of the channel-blocked
-    layout of the MFMA conv1."""
+    NHWC output and conv2 runs as an implicit GEMM over it, instead of the
+    fused conv1-in-conv2 kernel."""
     import dataclasses
     dims = dataclasses.replace(synth.DIMS_TINY, conv_channels=544, dtype="bf16")
     w = synth.make_weights(dims, 120)
@@ -266,6 +266,26 @@ def test_bf16_wide_stem_valu_conv1():
     out, taps = run_gpu(enc, clips, taps=True)
     rep = compare(dims, w, clips, out, taps)
     _print("wide stem", rep)
+    enc.free()
+
+
+@pytest.mark.parametrize("channels", [64, 288, 512])
+def test_bf16_fused_stem_widths(channels):
+    """The fused conv1-in-conv2 kernel at other stem widths: 2 slabs and one
+    partly filled 256-channel tile (64); a second output-channel tile holding
+    one 32-channel group, whose other waves see only padding rows (288); the
+    widest stem it takes, two full tiles and 16 slabs (512).  Clip lengths
+    give tail chunks and tiles at both ends of a chunk's 25 time columns."""
+    import dataclasses
+    dims = dataclasses.replace(synth.DIMS_TINY, conv_channels=channels, dtype="bf16")
+    w = synth.make_weights(dims, 140 + channels)
+    enc = make_encoder(dims, w)
+    lens = [16000 * 4 + 160 * 61 + 7, 16000 + 160 * 3]
+    clips = [synth.speech_like_clip(n, [96, i]) for i, n in enumerate(lens)]
+    _print(f"case: tiny bf16, {channels} stem channels", lens)
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(dims, w, clips, out, taps)
+    _print("fused stem width", rep)
     enc.free()
 
 
