@@ -54,6 +54,7 @@ namespace {
 constexpr int64_t kMaxSamples = 20LL * 60 * 16000;   // a request hears up to 20 minutes
 constexpr int64_t kMaxFullInput = 30LL * 16000;      // bounded input of full-input attention (30 s)
 constexpr int kHop = 160;
+constexpr int kSplitKMaxTokens = 4096;   // residual GEMMs of smaller batches take split-K
 constexpr int kNfft = 400;
 constexpr int kBins = kNfft / 2 + 1;
 
@@ -226,6 +227,9 @@ struct qa_encoder {
     int esize = 4;                      // bytes per operand element (4 fp32, 2 bf16)
     hipStream_t stream = nullptr;
     int device = 0;
+    // second lane of the layers (see run_encode): a stream and the fork/join events
+    hipStream_t lane = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // weights + constants in one device allocation
     char* wbuf = nullptr;
     size_t conv1_frag = 0;              // bf16 MFMA fragments of conv1 (0: VALU kernel)
@@ -493,10 +497,12 @@ QA_API qa_encoder* qa_encoder_create(const qa_weights* w, const qa_dims* d) {
     if (st == hipSuccess) st = hipMalloc(&e->wbuf, pk.host.size());
     if (st == hipSuccess) st = hipMemcpy(e->wbuf, pk.host.data(), pk.host.size(), hipMemcpyHostToDevice);
     if (st == hipSuccess) st = hipHostMalloc(&e->flag_host, sizeof(int), hipHostMallocDefault);
+    if (st == hipSuccess) st = hipStreamCreateWithFlags(&e->lane, hipStreamNonBlocking);
+    if (st == hipSuccess) st = hipEventCreateWithFlags(&e->ev_fork, hipEventDisableTiming);
+    if (st == hipSuccess) st = hipEventCreateWithFlags(&e->ev_join, hipEventDisableTiming);
     if (st != hipSuccess) {
         set_err("loading weights to the device failed: %s", hipGetErrorString(st));
-        if (e->wbuf) (void)hipFree(e->wbuf);
-        delete e;
+        qa_encoder_free(e);
         return nullptr;
     }
     return e;
@@ -574,6 +580,9 @@ QA_API void qa_encoder_free(qa_encoder* e) {
     if (e->pinned) (void)hipHostFree(e->pinned);
     if (e->flag_host) (void)hipHostFree(e->flag_host);
     for (hipEvent_t ev : e->ev_pool) (void)hipEventDestroy(ev);
+    if (e->lane) (void)hipStreamDestroy(e->lane);
+    if (e->ev_fork) (void)hipEventDestroy(e->ev_fork);
+    if (e->ev_join) (void)hipEventDestroy(e->ev_join);
     delete e;
 }
 
@@ -663,7 +672,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     const size_t o_u = slot((size_t)n_tok * std::max(F, D) * sizeof(T));
     // split-K partial sums of the residual GEMMs (small batches only: up to
     // 8 splits of [n_tok][D] fp32)
-    const size_t part_elems = n_tok <= 4096 ? (size_t)8 * n_tok * D : 0;
+    const size_t part_elems = n_tok <= kSplitKMaxTokens ? (size_t)8 * n_tok * D : 0;
     const size_t o_part = slot(part_elems * 4);
     size_t o_tstem = 0, o_tl0 = 0;
     if (taps) {
@@ -779,28 +788,76 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     if (!fused_stem)   // NHWC conv1 output (VALU conv1)
         QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1, n_chunks, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b), c2, false));
     QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2, n_chunks, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b), c3, true));
-    QA_LAUNCH("conv_out", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), x, nullptr,
-                                          part, part_elems));
     if (taps)
         QA_LAUNCH("tap_stem", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), tl0, tstem,
                                               part, part_elems));
-    for (int l = 0; l < d.n_layers; ++l) {
-        const LayerW& lw = e->layers[l];
-        QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b), h));
-        QA_LAUNCH("qkv", qa::gemm_bias<T>(s, h, n_tok, D, e->W<T>(lw.qkv_w), 3 * D, e->W<float>(lw.qkv_b), qkv, false));
-        QA_LAUNCH("attention", qa::attention<T>(s, qkv, d_cu, n_win, d.n_heads, D, max_seg, att));
-        QA_LAUNCH("o_proj", qa::gemm_bias_resid<T>(s, att, n_tok, D, e->W<T>(lw.o_w), D, e->W<float>(lw.o_b), x,
-                                                   part, part_elems));
-        QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b), h));
-        QA_LAUNCH("fc1", qa::gemm_bias<T>(s, h, n_tok, D, e->W<T>(lw.fc1_w), F, e->W<float>(lw.fc1_b), u, true));
-        QA_LAUNCH("fc2", qa::gemm_bias_resid<T>(s, u, n_tok, F, e->W<T>(lw.fc2_w), D, e->W<float>(lw.fc2_b), x,
-                                                part, part_elems));
-        if (l == 0 && taps)
-            QA_LAUNCH("tap_layer0", hipMemcpyAsync(tl0, x, (size_t)n_tok * D * 4, hipMemcpyDeviceToDevice, s));
+    // From conv_out on, a large batch runs as two lanes: the tokens split at the
+    // attention window whose start is nearest the middle, and each half runs
+    // conv_out, the layers and the projection on a stream of its own (the
+    // caller's and the encoder's second stream).  One half's tiles then fill
+    // the CUs that the other half's last round of tiles leaves idle.  Rows are
+    // independent in every kernel and no window crosses the split, so the
+    // outputs are bit-identical to one lane's.  Not with taps or profiling
+    // (one lane: each kernel's time is its own), nor for the small batches
+    // that take split-K (one workspace for the partial sums).
+    const int lanes = (!taps && !profiling && n_tok > kSplitKMaxTokens && n_win >= 2) ? 2 : 1;
+    int wsplit = n_win;
+    if (lanes == 2) {
+        wsplit = 1;
+        for (int w = 2; w < n_win; ++w)
+            if (std::abs(2 * (int64_t)cu[w] - n_tok) < std::abs(2 * (int64_t)cu[wsplit] - n_tok)) wsplit = w;
+        QA_LAUNCH("fork", hipEventRecord(e->ev_fork, s));
+        QA_LAUNCH("fork", hipStreamWaitEvent(e->lane, e->ev_fork, 0));
     }
-    QA_LAUNCH("ln", qa::layernorm<T>(s, x, n_tok, D, e->W<float>(e->post_ln_w), e->W<float>(e->post_ln_b), h));
-    QA_LAUNCH("proj1", qa::gemm_bias<T>(s, h, n_tok, D, e->W<T>(e->proj1_w), D, e->W<float>(e->proj1_b), u, true));
-    QA_LAUNCH("proj2", qa::gemm_bias_f32<T>(s, u, n_tok, D, e->W<T>(e->proj2_w), O, e->W<float>(e->proj2_b), out));
+    const int gw[3] = {0, wsplit, n_win};
+    const hipStream_t gs[2] = {s, e->lane};
+    float* gpart = lanes == 2 ? nullptr : part;
+    const size_t gpe = lanes == 2 ? 0 : part_elems;
+    const int UF = std::max(F, D);
+    // layer l of lane g; l == -1: conv_out, l == n_layers: the final LN and projection
+    for (int l = -1; l <= d.n_layers; ++l) {
+        for (int g = 0; g < lanes; ++g) {
+            const hipStream_t s = gs[g];
+            const int w0 = gw[g], nw = gw[g + 1] - w0, t0 = cu[w0], nt = cu[gw[g + 1]] - t0;
+            float* xg = x + (size_t)t0 * D;
+            T* hg = h + (size_t)t0 * D;
+            T* qg = qkv + (size_t)t0 * 3 * D;
+            T* ag = att + (size_t)t0 * D;
+            T* ug = u + (size_t)t0 * UF;   // fc1 rows of F, the projection's of D
+            if (l < 0) {
+                QA_LAUNCH("conv_out", qa::conv_out<T>(s, c3, d_src + t0, nt, 16 * C, e->W<T>(e->conv_out_w), D,
+                                                      e->W<float>(e->pe), xg, nullptr, gpart, gpe, lanes));
+                continue;
+            }
+            if (l == d.n_layers) {
+                QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(e->post_ln_w), e->W<float>(e->post_ln_b), hg));
+                QA_LAUNCH("proj1", qa::gemm_bias<T>(s, hg, nt, D, e->W<T>(e->proj1_w), D, e->W<float>(e->proj1_b), ug,
+                                                    true, lanes));
+                QA_LAUNCH("proj2", qa::gemm_bias_f32<T>(s, ug, nt, D, e->W<T>(e->proj2_w), O, e->W<float>(e->proj2_b),
+                                                        out + (size_t)t0 * O, lanes));
+                continue;
+            }
+            const LayerW& lw = e->layers[l];
+            QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b), hg));
+            QA_LAUNCH("qkv", qa::gemm_bias<T>(s, hg, nt, D, e->W<T>(lw.qkv_w), 3 * D, e->W<float>(lw.qkv_b), qg, false,
+                                              lanes));
+            // window offsets are absolute token rows
+            QA_LAUNCH("attention", qa::attention<T>(s, qkv, d_cu + w0, nw, d.n_heads, D, max_seg, att));
+            QA_LAUNCH("o_proj", qa::gemm_bias_resid<T>(s, ag, nt, D, e->W<T>(lw.o_w), D, e->W<float>(lw.o_b), xg,
+                                                       gpart, gpe, lanes));
+            QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b), hg));
+            QA_LAUNCH("fc1", qa::gemm_bias<T>(s, hg, nt, D, e->W<T>(lw.fc1_w), F, e->W<float>(lw.fc1_b), ug, true,
+                                              lanes));
+            QA_LAUNCH("fc2", qa::gemm_bias_resid<T>(s, ug, nt, F, e->W<T>(lw.fc2_w), D, e->W<float>(lw.fc2_b), xg,
+                                                    gpart, gpe, lanes));
+            if (l == 0 && taps)
+                QA_LAUNCH("tap_layer0", hipMemcpyAsync(tl0, x, (size_t)n_tok * D * 4, hipMemcpyDeviceToDevice, s));
+        }
+    }
+    if (lanes == 2) {
+        QA_LAUNCH("join", hipEventRecord(e->ev_join, e->lane));
+        QA_LAUNCH("join", hipStreamWaitEvent(s, e->ev_join, 0));
+    }
     QA_LAUNCH("flag", hipMemcpyAsync(e->flag_host, flag, sizeof(int), hipMemcpyDeviceToHost, s));
 #undef QA_LAUNCH
     hipError_t st = hipStreamSynchronize(s);

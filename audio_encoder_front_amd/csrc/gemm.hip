@@ -588,13 +588,15 @@ static hipError_t launch(hipStream_t s, const AL& al, int M, const T* w, int N, 
 
 // Tile choice: 256 x 256 with 8 waves of 128 x 64 (two waves per SIMD hide
 // LDS and MFMA latency) when the problem fills the GPU with it, else
-// 128 x 128 with 4 waves of 64 x 64.
+// 128 x 128 with 4 waves of 64 x 64.  `lanes` launches of the same shape
+// running side by side on separate streams fill it together.
 template <int SITE, typename T, class AL, class EP>
-static hipError_t run(hipStream_t s, const AL& al, int M, const T* w, int N, int K, const EP& ep) {
+static hipError_t run(hipStream_t s, const AL& al, int M, const T* w, int N, int K, const EP& ep,
+                      int lanes = 1) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if (K % Elem<T>::per16) return hipErrorInvalidValue;
     const long big = (long)((M + 255) / 256) * ((N + 255) / 256);
-    if (big >= 200) return launch<T, 256, 256, 2, 4, 128, SITE>(s, al, M, w, N, K, ep);
+    if (big * lanes >= 200) return launch<T, 256, 256, 2, 4, 128, SITE>(s, al, M, w, N, K, ep);
     return launch<T, 128, 128, 2, 2, 128, SITE>(s, al, M, w, N, K, ep);
 }
 
@@ -657,7 +659,7 @@ __global__ __launch_bounds__(256) void pe_reduce_kernel(float* __restrict__ x, f
 
 template <typename T>
 hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K, const T* w, int N,
-                    const float* pe, float* x, float* tap, float* part, size_t part_elems) {
+                    const float* pe, float* x, float* tap, float* part, size_t part_elems, int lanes) {
     GatherA<T> al{a, src, n_tok, K};
     if (n_tok <= 0 || N <= 0) return hipSuccess;
     const int sp = part ? resid_splits<T>(n_tok, K, N, part_elems) : 1;
@@ -671,16 +673,16 @@ hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K,
         return hipGetLastError();
     }
     EpiPE ep{x, tap, pe, src, n_tok, N};
-    return run<kConvOut>(s, al, n_tok, w, N, K, ep);
+    return run<kConvOut>(s, al, n_tok, w, N, K, ep, lanes);
 }
 
 template <typename T>
 hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N, const float* bias,
-                     T* out, bool gelu) {
+                     T* out, bool gelu, int lanes) {
     DenseA<T> al{a, M, K, K};
-    if (!gelu) return run<kQKV>(s, al, M, w, N, K, EpiBias<T, false>{out, bias, M, N});
-    if (N != K) return run<kFC1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N});
-    return run<kProj1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N});
+    if (!gelu) return run<kQKV>(s, al, M, w, N, K, EpiBias<T, false>{out, bias, M, N}, lanes);
+    if (N != K) return run<kFC1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N}, lanes);
+    return run<kProj1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N}, lanes);
 }
 
 // x[m][n] += bias[n] + (part[0][m][n] + part[1][m][n] + ...), the splits
@@ -706,7 +708,7 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(float* __restrict__ x
 
 template <typename T>
 hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, int N,
-                           const float* bias, float* x, float* part, size_t part_elems) {
+                           const float* bias, float* x, float* part, size_t part_elems, int lanes) {
     DenseA<T> al{a, M, K, K};
     if (M <= 0 || N <= 0) return hipSuccess;
     const int sp = part ? resid_splits<T>(M, K, N, part_elems) : 1;
@@ -721,16 +723,16 @@ hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, 
         return hipGetLastError();
     }
     EpiResid ep{x, bias, M, N};
-    if (N == K) return run<kOProj>(s, al, M, w, N, K, ep);
-    return run<kFC2>(s, al, M, w, N, K, ep);
+    if (N == K) return run<kOProj>(s, al, M, w, N, K, ep, lanes);
+    return run<kFC2>(s, al, M, w, N, K, ep, lanes);
 }
 
 template <typename T>
 hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, int N,
-                         const float* bias, float* out) {
+                         const float* bias, float* out, int lanes) {
     DenseA<T> al{a, M, K, K};
     EpiF32Bias ep{out, bias, M, N};
-    return run<kProj2>(s, al, M, w, N, K, ep);
+    return run<kProj2>(s, al, M, w, N, K, ep, lanes);
 }
 
 template <typename T>
@@ -759,13 +761,13 @@ hipError_t thinker_logits(hipStream_t s, const T* a, const int* rows, int n_rows
     template hipError_t conv3x3s2<T>(hipStream_t, const T*, int, int, int, int, const T*, const float*, \
                                      T*, bool);                                                       \
     template hipError_t conv_out<T>(hipStream_t, const T*, const int*, int, int, const T*, int,        \
-                                    const float*, float*, float*, float*, size_t);                                    \
+                                    const float*, float*, float*, float*, size_t, int);               \
     template hipError_t gemm_bias<T>(hipStream_t, const T*, int, int, const T*, int, const float*, T*, \
-                                     bool);                                                           \
+                                     bool, int);                                                      \
     template hipError_t gemm_bias_resid<T>(hipStream_t, const T*, int, int, const T*, int,            \
-                                           const float*, float*, float*, size_t);                     \
+                                           const float*, float*, float*, size_t, int);                \
     template hipError_t gemm_bias_f32<T>(hipStream_t, const T*, int, int, const T*, int, const float*, \
-                                         float*);
+                                         float*, int);
 template hipError_t thinker_gemm<float>(hipStream_t, int, const float*, int, int, const float*, int, const float*,
                                         float*, float*);
 template hipError_t thinker_gemm<bf16>(hipStream_t, int, const bf16*, int, int, const bf16*, int, const float*,

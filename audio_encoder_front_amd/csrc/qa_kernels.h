@@ -85,22 +85,27 @@ hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win,
 // tap[t][:] without the PE.
 // part (part_elems floats, may be null): workspace for split-K, used when
 // the batch is too small to fill the GPU with tiles.
+// lanes (all GEMMs here): how many launches of this shape the caller runs side
+// by side on separate streams; the 256 x 256 tiling is taken when lanes times
+// its tile count fills the GPU.  It changes the tiling only, never a value.
 template <typename T>
 hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K, const T* w, int N,
-                    const float* pe, float* x, float* tap, float* part = nullptr, size_t part_elems = 0);
+                    const float* pe, float* x, float* tap, float* part = nullptr, size_t part_elems = 0,
+                    int lanes = 1);
 
 // ---- dense GEMMs: out[M][N] = A[M][K] . W[N][K]^T + bias
 template <typename T>
 hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N, const float* bias,
-                     T* out, bool gelu);
+                     T* out, bool gelu, int lanes = 1);
 // x += A . W^T + bias.  part (part_elems floats, may be null): workspace for
 // split-K, used when the batch is too small to fill the GPU with tiles.
 template <typename T>
 hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, int N,
-                           const float* bias, float* x, float* part = nullptr, size_t part_elems = 0);
+                           const float* bias, float* x, float* part = nullptr, size_t part_elems = 0,
+                           int lanes = 1);
 template <typename T>
 hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, int N,
-                         const float* bias, float* out);
+                         const float* bias, float* out, int lanes = 1);
 
 // ---- LayerNorm (fp32 in, T out) and windowed attention
 template <typename T>

@@ -131,7 +131,11 @@ int64_t qa_encode_num_tokens(int64_t n_samples);
 qa_encoder *qa_encoder_create(const qa_weights *w, const qa_dims *d);
 
 /* Enqueue all later work of this handle on `hip_stream` (a hipStream_t;
- * NULL = the null stream).  Returns QA_STATUS_OK or INVALID_PARAMS. */
+ * NULL = the null stream).  A batch of more than 4,096 tokens also runs half
+ * of its layers on a second stream the handle owns (created with it, default
+ * priority), forked from and joined back into `hip_stream` by events inside
+ * the call, so that later work on `hip_stream` sees every result.  Returns
+ * QA_STATUS_OK or INVALID_PARAMS. */
 int qa_encoder_set_stream(qa_encoder *e, void *hip_stream);
 
 /* Encode a packed batch: every step of the tower above, one packed forward
@@ -184,7 +188,8 @@ int qa_encode(qa_encoder *e, const float *pcm, const int64_t *lengths, int n_cli
 int qa_encode_noalloc(qa_encoder *e, const float *pcm, const int64_t *lengths, int n_clips, float *out);
 
 /* Keep stage outputs of later qa_encode calls for qa_encoder_tap (costs one
- * extra conv_out GEMM and a copy per call).  enable: 0 or 1. */
+ * extra conv_out GEMM and a copy per call, and runs the layers on the
+ * handle's stream alone; the outputs are bit-identical).  enable: 0 or 1. */
 int qa_encoder_enable_taps(qa_encoder *e, int enable);
 
 /* Copy tap `tap` (QA_TAP_*) of the last qa_encode into the DEVICE buffer dst
@@ -194,7 +199,8 @@ int qa_encoder_enable_taps(qa_encoder *e, int enable);
 int64_t qa_encoder_tap(qa_encoder *e, int tap, float *dst, int64_t capacity);
 
 /* Per-kernel timing with HIP events recorded on the handle's stream around
- * every launch (0 disables; the default).  qa_encoder_kernel_times fills up
+ * every launch (0 disables; the default).  While it is on, every kernel runs
+ * on the handle's stream alone, so that each time is that kernel's own.  qa_encoder_kernel_times fills up
  * to `cap` entries of: a static NUL-terminated label, the summed
  * milliseconds and the launch count accumulated since profiling was last
  * enabled, and returns the number of labels (which may exceed cap). */

@@ -175,6 +175,9 @@ def test_b06_packed_32_clips(b06):
     clips = synth.make_audio(wl32)
     _print("case: 0.6B bf16, 32 clips U(1,30) s")
     out, taps = run_gpu(enc, clips, taps=True)
+    # without taps the batch (5,986 tokens) runs as two lanes: bit-identical
+    out2, _ = run_gpu(enc, clips)
+    assert np.array_equal(out2, out)
     # every window of every clip (73), per window and per row, and the
     # log-mel of every clip
     rep = compare(wl.dims, w, clips, out, taps, progress="b06_32")
@@ -214,6 +217,8 @@ def test_b17_twenty_minutes_every_window(b17):
     out, taps = run_gpu(enc, clips, taps=True)
     assert out.shape == (15600, 2048)
     assert np.all(np.isfinite(out))
+    out2, _ = run_gpu(enc, clips)        # two lanes (no taps): bit-identical
+    assert np.array_equal(out2, out)
     rep = compare(wl.dims, w, clips, out, taps, progress="b17_20m")
     assert rep["windows_checked"] == 150
     _print("b17_20m", rep)
@@ -225,12 +230,33 @@ def test_b17_packed_16_clips_every_window(b17):
     _print("case: 1.7B bf16, 16 clips logU(10,300) s (every window)")
     out, taps = run_gpu(enc, clips, taps=True)
     assert out.shape == (21162, 2048)
+    out2, _ = run_gpu(enc, clips)        # two lanes (no taps): bit-identical
+    assert np.array_equal(out2, out)
     rep = compare(wl.dims, w, clips, out, taps, progress="b17_16")
     assert rep["windows_checked"] == 213
     _print("b17_16", rep)
     rows = tail_reading_check(wl.dims, w, clips, taps)
     _print("b17_16 tail rows", rows)
     assert len(rows) >= 8
+
+
+def test_two_lanes_fp32(tiny):
+    """Batches past the split-K sizes run conv_out, the layers and the
+    projection as two lanes on two streams, split at the window whose start
+    is nearest the middle (here token 2,184 of 4,292, inside the 300 s clip);
+    with taps on they run as one.  The two runs are bit-identical, and the
+    windows at the split, the ends and the second clip match the oracle."""
+    wl, _, w, enc = tiny
+    lens = [16000 * 300, 16000 * 30 + 160 * 13 + 3]
+    clips = [synth.speech_like_clip(n, [97, i]) for i, n in enumerate(lens)]
+    _print("case: tiny fp32, two lanes", lens)
+    out2, _ = run_gpu(enc, clips)
+    out, taps = run_gpu(enc, clips, taps=True)
+    assert out.shape[0] == 4292
+    assert np.array_equal(out2, out)
+    rep = compare(wl.dims, w, clips, out, taps,
+                  windows_per_clip=lambda ci, nw: [0, 19, 20, 21, 22, nw - 1] if ci == 0 else range(nw))
+    _print("two lanes", rep)
 
 
 @pytest.mark.parametrize("base,window_chunks", [("tiny", 9), ("tiny", 1), ("b06", 9), ("b06", 1)])
