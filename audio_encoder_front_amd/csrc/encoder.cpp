@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <utility>
 #include <mutex>
 #include <new>
 #include <string>
@@ -814,6 +815,16 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     float* gpart = lanes == 2 ? nullptr : part;
     const size_t gpe = lanes == 2 ? 0 : part_elems;
     const int UF = std::max(F, D);
+    // The LayerNorm after a residual GEMM (conv_out, O-proj, FC2) runs inside
+    // that GEMM's split-K reduction when it splits K (small batches); ln_ready
+    // says that lane's h already holds the next LayerNorm's output.
+    bool ln_ready[2] = {false, false};
+    auto ln_of = [&](int l, bool second) -> std::pair<const float*, const float*> {
+        if (l >= d.n_layers) return {e->W<float>(e->post_ln_w), e->W<float>(e->post_ln_b)};
+        const LayerW& lw = e->layers[l];
+        return second ? std::make_pair(e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b))
+                      : std::make_pair(e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b));
+    };
     // layer l of lane g; l == -1: conv_out, l == n_layers: the final LN and projection
     for (int l = -1; l <= d.n_layers; ++l) {
         for (int g = 0; g < lanes; ++g) {
@@ -825,12 +836,16 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
             T* ag = att + (size_t)t0 * D;
             T* ug = u + (size_t)t0 * UF;   // fc1 rows of F, the projection's of D
             if (l < 0) {
+                const auto nx = ln_of(0, false);
+                qa::LnAfter<T> after{nx.first, nx.second, hg, false};
                 QA_LAUNCH("conv_out", qa::conv_out<T>(s, c3, d_src + t0, nt, 16 * C, e->W<T>(e->conv_out_w), D,
-                                                      e->W<float>(e->pe), xg, nullptr, gpart, gpe, lanes));
+                                                      e->W<float>(e->pe), xg, nullptr, gpart, gpe, lanes, &after));
+                ln_ready[g] = after.done;
                 continue;
             }
             if (l == d.n_layers) {
-                QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(e->post_ln_w), e->W<float>(e->post_ln_b), hg));
+                if (!ln_ready[g])
+                    QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(e->post_ln_w), e->W<float>(e->post_ln_b), hg));
                 QA_LAUNCH("proj1", qa::gemm_bias<T>(s, hg, nt, D, e->W<T>(e->proj1_w), D, e->W<float>(e->proj1_b), ug,
                                                     true, lanes));
                 QA_LAUNCH("proj2", qa::gemm_bias_f32<T>(s, ug, nt, D, e->W<T>(e->proj2_w), O, e->W<float>(e->proj2_b),
@@ -838,18 +853,24 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
                 continue;
             }
             const LayerW& lw = e->layers[l];
-            QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b), hg));
+            if (!ln_ready[g])
+                QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b), hg));
             QA_LAUNCH("qkv", qa::gemm_bias<T>(s, hg, nt, D, e->W<T>(lw.qkv_w), 3 * D, e->W<float>(lw.qkv_b), qg, false,
                                               lanes));
             // window offsets are absolute token rows
             QA_LAUNCH("attention", qa::attention<T>(s, qkv, d_cu + w0, nw, d.n_heads, D, max_seg, att));
+            qa::LnAfter<T> after2{e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b), hg, false};
             QA_LAUNCH("o_proj", qa::gemm_bias_resid<T>(s, ag, nt, D, e->W<T>(lw.o_w), D, e->W<float>(lw.o_b), xg,
-                                                       gpart, gpe, lanes));
-            QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b), hg));
+                                                       gpart, gpe, lanes, &after2));
+            if (!after2.done)
+                QA_LAUNCH("ln", qa::layernorm<T>(s, xg, nt, D, e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b), hg));
             QA_LAUNCH("fc1", qa::gemm_bias<T>(s, hg, nt, D, e->W<T>(lw.fc1_w), F, e->W<float>(lw.fc1_b), ug, true,
                                               lanes));
+            const auto nx = ln_of(l + 1, false);
+            qa::LnAfter<T> after1{nx.first, nx.second, hg, false};
             QA_LAUNCH("fc2", qa::gemm_bias_resid<T>(s, ug, nt, F, e->W<T>(lw.fc2_w), D, e->W<float>(lw.fc2_b), xg,
-                                                    gpart, gpe, lanes));
+                                                    gpart, gpe, lanes, &after1));
+            ln_ready[g] = after1.done;
             if (l == 0 && taps)
                 QA_LAUNCH("tap_layer0", hipMemcpyAsync(tl0, x, (size_t)n_tok * D * 4, hipMemcpyDeviceToDevice, s));
         }

@@ -620,6 +620,8 @@ hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win,
 // `part`, and a reduction kernel adds them in a fixed order and applies the
 // epilogue (resid_reduce: into the residual; pe_reduce: plus the position
 // table).  Returns the number of splits (1: none).
+constexpr int kMaxSplits = 8;
+
 template <typename T>
 static int resid_splits(int M, int K, int N, size_t part_elems) {
     constexpr int KSTEP = 128 / (int)sizeof(T);
@@ -627,7 +629,7 @@ static int resid_splits(int M, int K, int N, size_t part_elems) {
     const long big = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
     if (big >= 200 || tiles >= 128 || nk < 8 || N % 4) return 1;
-    int sp = (int)std::min<long>(8, 256 / tiles);
+    int sp = (int)std::min<long>(kMaxSplits, 256 / tiles);
     sp = std::min(sp, nk / 4);
     if (sp < 2) return 1;
     const int kper = (nk + sp - 1) / sp;
@@ -657,34 +659,6 @@ __global__ __launch_bounds__(256) void pe_reduce_kernel(float* __restrict__ x, f
     if (tap) *reinterpret_cast<float4*>(tap + o) = acc;
 }
 
-template <typename T>
-hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K, const T* w, int N,
-                    const float* pe, float* x, float* tap, float* part, size_t part_elems, int lanes) {
-    GatherA<T> al{a, src, n_tok, K};
-    if (n_tok <= 0 || N <= 0) return hipSuccess;
-    const int sp = part ? resid_splits<T>(n_tok, K, N, part_elems) : 1;
-    if (sp > 1) {   // split-K (see resid_splits), the PE added in the reduction
-        if (K % Elem<T>::per16) return hipErrorInvalidValue;
-        const hipError_t st =
-            launch<T, 128, 128, 2, 2, 128, kConvOut>(s, al, n_tok, w, N, K, EpiPartial{part, n_tok, N}, sp);
-        if (st != hipSuccess) return st;
-        const unsigned blocks = (unsigned)(((int64_t)n_tok * (N / 4) + 255) / 256);
-        pe_reduce_kernel<<<blocks, 256, 0, s>>>(x, tap, part, sp, n_tok, N, pe, src);
-        return hipGetLastError();
-    }
-    EpiPE ep{x, tap, pe, src, n_tok, N};
-    return run<kConvOut>(s, al, n_tok, w, N, K, ep, lanes);
-}
-
-template <typename T>
-hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N, const float* bias,
-                     T* out, bool gelu, int lanes) {
-    DenseA<T> al{a, M, K, K};
-    if (!gelu) return run<kQKV>(s, al, M, w, N, K, EpiBias<T, false>{out, bias, M, N}, lanes);
-    if (N != K) return run<kFC1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N}, lanes);
-    return run<kProj1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N}, lanes);
-}
-
 // x[m][n] += bias[n] + (part[0][m][n] + part[1][m][n] + ...), the splits
 // added in a fixed order (deterministic), 4 values per thread.
 __global__ __launch_bounds__(256) void resid_reduce_kernel(float* __restrict__ x, const float* __restrict__ part,
@@ -706,9 +680,111 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(float* __restrict__ x
     *px = make_float4(r.x + (b.x + acc.x), r.y + (b.y + acc.y), r.z + (b.z + acc.z), r.w + (b.w + acc.w));
 }
 
+// The split-K reductions with the LayerNorm that follows them fused in: one
+// wave per row, the splits added in the same order as resid_reduce_kernel
+// (PE = false: x += bias + sum) or pe_reduce_kernel (PE = true: x = sum +
+// pe, tap = sum), then ln = LayerNorm(x) through the same row routine as
+// layernorm.  Both results are bit-identical to the two kernels run one
+// after the other; the row stays in registers between them.
+template <typename T, int NQ, bool PE>
+__global__ __launch_bounds__(256) void reduce_ln_kernel(float* __restrict__ x, float* __restrict__ tap,
+                                                        const float* __restrict__ part, int splits, int M, int N,
+                                                        const float* __restrict__ add, const int* __restrict__ src,
+                                                        const float* __restrict__ g, const float* __restrict__ b,
+                                                        T* __restrict__ ln) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const int n4 = N >> 2;
+    const size_t plane = (size_t)M * N;
+    const float* addr = PE ? add + (size_t)(src[m] % kChunkTok) * N : add;
+    // every split of the row in flight at once (one wave holds a whole row)
+    float4 p[NQ][kMaxSplits];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int i = lane + 64 * q;
+        if (i >= n4) continue;
+        const float* pq = part + (size_t)m * N + 4 * i;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < splits) p[q][sp] = *reinterpret_cast<const float4*>(pq + sp * plane);
+    }
+    float4 v[NQ], gg[NQ], bb[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int i = lane + 64 * q;
+        if (i >= n4) continue;
+        float4 acc = p[q][0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxSplits; ++sp)
+            if (sp < splits) { acc.x += p[q][sp].x; acc.y += p[q][sp].y; acc.z += p[q][sp].z; acc.w += p[q][sp].w; }
+        const size_t o = (size_t)m * N + 4 * i;
+        const float4 a4 = reinterpret_cast<const float4*>(addr)[i];
+        float4* px = reinterpret_cast<float4*>(x + o);
+        if constexpr (PE) {
+            v[q] = make_float4(acc.x + a4.x, acc.y + a4.y, acc.z + a4.z, acc.w + a4.w);
+            if (tap) *reinterpret_cast<float4*>(tap + o) = acc;
+        } else {
+            const float4 r = *px;
+            v[q] = make_float4(r.x + (a4.x + acc.x), r.y + (a4.y + acc.y), r.z + (a4.z + acc.z), r.w + (a4.w + acc.w));
+        }
+        *px = v[q];
+        gg[q] = reinterpret_cast<const float4*>(g)[i];
+        bb[q] = reinterpret_cast<const float4*>(b)[i];
+    }
+    ln_row<T, NQ>(v, gg, bb, lane, N, ln + (size_t)m * N);
+}
+
+// The reduction of a split-K residual GEMM (PE: conv_out's), with the
+// following LayerNorm fused in when `after` asks for one and the row fits.
+template <typename T, bool PE>
+static hipError_t reduce_split(hipStream_t s, float* x, float* tap, const float* part, int sp, int M, int N,
+                               const float* add, const int* src, LnAfter<T>* after) {
+    if (after && N % 4 == 0 && N <= 1024 && sp <= kMaxSplits) {
+        reduce_ln_kernel<T, 4, PE><<<(unsigned)((M + 3) / 4), 256, 0, s>>>(x, tap, part, sp, M, N, add, src,
+                                                                          after->g, after->b, after->out);
+        after->done = true;
+    } else if (PE) {
+        const unsigned blocks = (unsigned)(((int64_t)M * (N / 4) + 255) / 256);
+        pe_reduce_kernel<<<blocks, 256, 0, s>>>(x, tap, part, sp, M, N, add, src);
+    } else {
+        const int64_t groups = (int64_t)M * (N / 4);
+        resid_reduce_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(x, part, sp, M, N, add);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K, const T* w, int N,
+                    const float* pe, float* x, float* tap, float* part, size_t part_elems, int lanes,
+                    LnAfter<T>* after) {
+    GatherA<T> al{a, src, n_tok, K};
+    if (n_tok <= 0 || N <= 0) return hipSuccess;
+    const int sp = part ? resid_splits<T>(n_tok, K, N, part_elems) : 1;
+    if (sp > 1) {   // split-K (see resid_splits), the PE added in the reduction
+        if (K % Elem<T>::per16) return hipErrorInvalidValue;
+        const hipError_t st =
+            launch<T, 128, 128, 2, 2, 128, kConvOut>(s, al, n_tok, w, N, K, EpiPartial{part, n_tok, N}, sp);
+        if (st != hipSuccess) return st;
+        return reduce_split<T, true>(s, x, tap, part, sp, n_tok, N, pe, src, after);
+    }
+    EpiPE ep{x, tap, pe, src, n_tok, N};
+    return run<kConvOut>(s, al, n_tok, w, N, K, ep, lanes);
+}
+
+template <typename T>
+hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N, const float* bias,
+                     T* out, bool gelu, int lanes) {
+    DenseA<T> al{a, M, K, K};
+    if (!gelu) return run<kQKV>(s, al, M, w, N, K, EpiBias<T, false>{out, bias, M, N}, lanes);
+    if (N != K) return run<kFC1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N}, lanes);
+    return run<kProj1>(s, al, M, w, N, K, EpiBias<T, true>{out, bias, M, N}, lanes);
+}
+
 template <typename T>
 hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, int N,
-                           const float* bias, float* x, float* part, size_t part_elems, int lanes) {
+                           const float* bias, float* x, float* part, size_t part_elems, int lanes,
+                           LnAfter<T>* after) {
     DenseA<T> al{a, M, K, K};
     if (M <= 0 || N <= 0) return hipSuccess;
     const int sp = part ? resid_splits<T>(M, K, N, part_elems) : 1;
@@ -718,9 +794,7 @@ hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, 
         const hipError_t st = N == K ? launch<T, 128, 128, 2, 2, 128, kOProj>(s, al, M, w, N, K, ep, sp)
                                      : launch<T, 128, 128, 2, 2, 128, kFC2>(s, al, M, w, N, K, ep, sp);
         if (st != hipSuccess) return st;
-        const int64_t groups = (int64_t)M * (N / 4);
-        resid_reduce_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(x, part, sp, M, N, bias);
-        return hipGetLastError();
+        return reduce_split<T, false>(s, x, nullptr, part, sp, M, N, bias, nullptr, after);
     }
     EpiResid ep{x, bias, M, N};
     if (N == K) return run<kOProj>(s, al, M, w, N, K, ep, lanes);
@@ -761,11 +835,11 @@ hipError_t thinker_logits(hipStream_t s, const T* a, const int* rows, int n_rows
     template hipError_t conv3x3s2<T>(hipStream_t, const T*, int, int, int, int, const T*, const float*, \
                                      T*, bool);                                                       \
     template hipError_t conv_out<T>(hipStream_t, const T*, const int*, int, int, const T*, int,        \
-                                    const float*, float*, float*, float*, size_t, int);               \
+                                    const float*, float*, float*, float*, size_t, int, LnAfter<T>*);  \
     template hipError_t gemm_bias<T>(hipStream_t, const T*, int, int, const T*, int, const float*, T*, \
                                      bool, int);                                                      \
     template hipError_t gemm_bias_resid<T>(hipStream_t, const T*, int, int, const T*, int,            \
-                                           const float*, float*, float*, size_t, int);                \
+                                           const float*, float*, float*, size_t, int, LnAfter<T>*);   \
     template hipError_t gemm_bias_f32<T>(hipStream_t, const T*, int, int, const T*, int, const float*, \
                                          float*, int);
 template hipError_t thinker_gemm<float>(hipStream_t, int, const float*, int, int, const float*, int, const float*,

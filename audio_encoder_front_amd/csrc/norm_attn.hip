@@ -21,14 +21,6 @@ namespace qa {
 
 // ------------------------------------------------------------ LayerNorm
 
-constexpr float kLnEps = 1e-5f;
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 template <typename T, int NQ>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, int M, int d,
                                                         const float* __restrict__ g,
@@ -62,32 +54,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
     }
     for (; row < M; row += stride) {
         if (row + stride < M) load_row(row + stride, nxt);
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int i = lane + 64 * q;
-            if (i < d4) s += (cur[q].x + cur[q].y) + (cur[q].z + cur[q].w);
-        }
-        const float mean = wave_sum(s) / (float)d;
-        float ss = 0.f;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int i = lane + 64 * q;
-            if (i < d4) {
-                const float a = cur[q].x - mean, e1 = cur[q].y - mean, c = cur[q].z - mean, e = cur[q].w - mean;
-                ss += (a * a + e1 * e1) + (c * c + e * e);
-            }
-        }
-        const float rstd = rsqrtf(wave_sum(ss) / (float)d + kLnEps);
-        T* o = out + (size_t)row * d;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int i = lane + 64 * q;
-            if (i < d4)
-                store4(o + 4 * i, (cur[q].x - mean) * rstd * gg[q].x + bb[q].x,
-                       (cur[q].y - mean) * rstd * gg[q].y + bb[q].y, (cur[q].z - mean) * rstd * gg[q].z + bb[q].z,
-                       (cur[q].w - mean) * rstd * gg[q].w + bb[q].w);
-        }
+        ln_row<T, NQ>(cur, gg, bb, lane, d, out + (size_t)row * d);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) cur[q] = nxt[q];
     }

@@ -157,4 +157,47 @@ __device__ __forceinline__ float key_float(int k) {
     return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff));
 }
 
+// ---- LayerNorm of one row held by one wave (fp32 statistics)
+constexpr float kLnEps = 1e-5f;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Lane `lane` holds the row's float4 chunks i = lane + 64 q (q < NQ, i < d/4)
+// in v, and gamma / beta's in g / b; writes (v - mean) / sqrt(var + eps) *
+// gamma + beta to o[0 .. d).  Every LayerNorm of the encoder goes through
+// this one sequence, so a fused and a separate LayerNorm agree bit for bit.
+template <typename T, int NQ>
+__device__ __forceinline__ void ln_row(const float4 (&v)[NQ], const float4 (&g)[NQ], const float4 (&b)[NQ],
+                                       int lane, int d, T* __restrict__ o) {
+    const int d4 = d >> 2;
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int i = lane + 64 * q;
+        if (i < d4) s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
+    }
+    const float mean = wave_sum(s) / (float)d;
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int i = lane + 64 * q;
+        if (i < d4) {
+            const float a = v[q].x - mean, e1 = v[q].y - mean, c = v[q].z - mean, e = v[q].w - mean;
+            ss += (a * a + e1 * e1) + (c * c + e * e);
+        }
+    }
+    const float rstd = rsqrtf(wave_sum(ss) / (float)d + kLnEps);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int i = lane + 64 * q;
+        if (i < d4)
+            store4(o + 4 * i, (v[q].x - mean) * rstd * g[q].x + b[q].x, (v[q].y - mean) * rstd * g[q].y + b[q].y,
+                   (v[q].z - mean) * rstd * g[q].z + b[q].z, (v[q].w - mean) * rstd * g[q].w + b[q].w);
+    }
+}
+
 }  // namespace qa

@@ -88,10 +88,22 @@ hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win,
 // lanes (all GEMMs here): how many launches of this shape the caller runs side
 // by side on separate streams; the 256 x 256 tiling is taken when lanes times
 // its tile count fills the GPU.  It changes the tiling only, never a value.
+// after (conv_out, gemm_bias_resid; may be null): the LayerNorm that follows
+// (gamma g, beta b, output out [rows][N]).  When the GEMM splits K its
+// reduction also writes out = LayerNorm(x), bit-identical to layernorm on
+// the new x, and sets done; otherwise done is left false and the caller runs
+// layernorm itself.
+template <typename T>
+struct LnAfter {
+    const float* g;
+    const float* b;
+    T* out;
+    bool done;
+};
 template <typename T>
 hipError_t conv_out(hipStream_t s, const T* a, const int* src, int n_tok, int K, const T* w, int N,
                     const float* pe, float* x, float* tap, float* part = nullptr, size_t part_elems = 0,
-                    int lanes = 1);
+                    int lanes = 1, LnAfter<T>* after = nullptr);
 
 // ---- dense GEMMs: out[M][N] = A[M][K] . W[N][K]^T + bias
 template <typename T>
@@ -102,7 +114,7 @@ hipError_t gemm_bias(hipStream_t s, const T* a, int M, int K, const T* w, int N,
 template <typename T>
 hipError_t gemm_bias_resid(hipStream_t s, const T* a, int M, int K, const T* w, int N,
                            const float* bias, float* x, float* part = nullptr, size_t part_elems = 0,
-                           int lanes = 1);
+                           int lanes = 1, LnAfter<T>* after = nullptr);
 template <typename T>
 hipError_t gemm_bias_f32(hipStream_t s, const T* a, int M, int K, const T* w, int N,
                          const float* bias, float* out, int lanes = 1);
