@@ -777,26 +777,12 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     QA_LAUNCH("frontend", qa::frontend(s, pcm, d_clips, d_tiles, n_tiles, e->W<uint4>(e->basis), e->W<float>(e->melw),
                                        e->W<int>(e->melb0), logmel, key, flag));
     QA_LAUNCH("normalize", qa::normalize(s, logmel, d_clips, d_tiles, n_tiles, key));
-    if constexpr (std::is_same<T, qa::bf16>::value) {
-        if (fused_stem)
-            QA_LAUNCH("stem12", qa::stem12(s, logmel, d_chunks, n_chunks, e->W<uint4>(e->conv1_frag), e->W<T>(e->conv2_w),
-                                           e->W<float>(e->conv2_b), C, c2));
-        else
-            QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
-    } else {
-        QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
-    }
-    if (!fused_stem)   // NHWC conv1 output (VALU conv1)
-        QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1, n_chunks, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b), c2, false));
-    QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2, n_chunks, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b), c3, true));
-    if (taps)
-        QA_LAUNCH("tap_stem", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D, e->W<float>(e->pe), tl0, tstem,
-                                              part, part_elems));
-    // From conv_out on, a large batch runs as two lanes: the tokens split at the
-    // attention window whose start is nearest the middle, and each half runs
-    // conv_out, the layers and the projection on a stream of its own (the
-    // caller's and the encoder's second stream).  One half's tiles then fill
-    // the CUs that the other half's last round of tiles leaves idle.  Rows are
+    // From the stem on, a large batch runs as two lanes: the tokens split at
+    // the attention window whose start is nearest the middle (a chunk
+    // boundary), and each half runs its stem chunks, conv_out, the layers and
+    // the projection on a stream of its own (the caller's and the encoder's
+    // second stream).  One half's tiles then fill the CUs that the other
+    // half's last round of tiles leaves idle.  Rows (chunks, tokens) are
     // independent in every kernel and no window crosses the split, so the
     // outputs are bit-identical to one lane's.  Not with taps or profiling
     // (one lane: each kernel's time is its own), nor for the small batches
@@ -825,11 +811,38 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
         return second ? std::make_pair(e->W<float>(lw.ln2_w), e->W<float>(lw.ln2_b))
                       : std::make_pair(e->W<float>(lw.ln1_w), e->W<float>(lw.ln1_b));
     };
-    // layer l of lane g; l == -1: conv_out, l == n_layers: the final LN and projection
-    for (int l = -1; l <= d.n_layers; ++l) {
+    // layer l of lane g; l == -2: the stem, -1: conv_out, n_layers: the final LN and projection
+    for (int l = -2; l <= d.n_layers; ++l) {
         for (int g = 0; g < lanes; ++g) {
             const hipStream_t s = gs[g];
             const int w0 = gw[g], nw = gw[g + 1] - w0, t0 = cu[w0], nt = cu[gw[g + 1]] - t0;
+            if (l == -2) {   // the lane's chunks: windows start at chunk boundaries
+                const int k0 = tok_src[t0] / qa::kChunkTok;
+                const int nk = (g + 1 < lanes ? tok_src[cu[gw[g + 1]]] / qa::kChunkTok : n_chunks) - k0;
+                const qa::ChunkInfo* dk = d_chunks + k0;
+                T* c1g = c1 + (size_t)k0 * 64 * 50 * C;
+                T* c2g = c2 + (size_t)k0 * 32 * 25 * C;
+                if constexpr (std::is_same<T, qa::bf16>::value) {
+                    if (fused_stem)
+                        QA_LAUNCH("stem12", qa::stem12(s, logmel, dk, nk, e->W<uint4>(e->conv1_frag), e->W<T>(e->conv2_w),
+                                                       e->W<float>(e->conv2_b), C, c2g));
+                    else
+                        QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, dk, nk, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b),
+                                                        C, c1g));
+                } else {
+                    QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, dk, nk, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C,
+                                                    c1g));
+                }
+                if (!fused_stem)   // NHWC conv1 output (VALU conv1)
+                    QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1g, nk, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b),
+                                                        c2g, false, lanes));
+                QA_LAUNCH("conv3", qa::conv3x3s2<T>(s, c2g, nk, 32, 25, C, e->W<T>(e->conv3_w), e->W<float>(e->conv3_b),
+                                                    c3 + (size_t)k0 * 13 * 16 * C, true, lanes));
+                if (taps)   // one lane
+                    QA_LAUNCH("tap_stem", qa::conv_out<T>(s, c3, d_src, n_tok, 16 * C, e->W<T>(e->conv_out_w), D,
+                                                          e->W<float>(e->pe), tl0, tstem, part, part_elems));
+                continue;
+            }
             float* xg = x + (size_t)t0 * D;
             T* hg = h + (size_t)t0 * D;
             T* qg = qkv + (size_t)t0 * 3 * D;

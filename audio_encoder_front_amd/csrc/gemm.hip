@@ -604,14 +604,14 @@ static hipError_t run(hipStream_t s, const AL& al, int M, const T* w, int N, int
 
 template <typename T>
 hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win, int C,
-                     const T* w, const float* bias, T* out, bool time_major) {
+                     const T* w, const float* bias, T* out, bool time_major, int lanes) {
     const int Hout = (Hin + 1) / 2, Wout = (Win + 1) / 2;
     const int M = n_chunks * Hout * Wout;
     if (C % kConvCB) return hipErrorInvalidValue;
     ConvA<T> al{in, M, Hin, Win, C, Hout, Wout, time_major};
     EpiBias<T, true> ep{out, bias, M, C};
     if (C % Elem<T>::per16) return hipErrorInvalidValue;
-    return time_major ? run<kConv3>(s, al, M, w, C, 9 * C, ep) : run<kConv2>(s, al, M, w, C, 9 * C, ep);
+    return time_major ? run<kConv3>(s, al, M, w, C, 9 * C, ep, lanes) : run<kConv2>(s, al, M, w, C, 9 * C, ep, lanes);
 }
 
 // Split-K for the residual GEMMs and conv_out of small batches: when the
@@ -833,7 +833,7 @@ hipError_t thinker_logits(hipStream_t s, const T* a, const int* rows, int n_rows
 
 #define QA_INST(T)                                                                                    \
     template hipError_t conv3x3s2<T>(hipStream_t, const T*, int, int, int, int, const T*, const float*, \
-                                     T*, bool);                                                       \
+                                     T*, bool, int);                                                  \
     template hipError_t conv_out<T>(hipStream_t, const T*, const int*, int, int, const T*, int,        \
                                     const float*, float*, float*, float*, size_t, int, LnAfter<T>*);  \
     template hipError_t gemm_bias<T>(hipStream_t, const T*, int, int, const T*, int, const float*, T*, \

@@ -80,7 +80,7 @@ hipError_t stem12(hipStream_t s, const float* logmel, const ChunkInfo* chunks, i
 // [n_chunks][Hout][Wout][C] (time_major=false) or [n_chunks][Wout][Hout][C].
 template <typename T>
 hipError_t conv3x3s2(hipStream_t s, const T* in, int n_chunks, int Hin, int Win, int C,
-                     const T* w, const float* bias, T* out, bool time_major);
+                     const T* w, const float* bias, T* out, bool time_major, int lanes = 1);
 // x[t][:] = A[src[t]][:] . Wout^T + pe[src[t] % 13][:]  (fp32), and optionally
 // tap[t][:] without the PE.
 // part (part_elems floats, may be null): workspace for split-K, used when
