@@ -745,7 +745,8 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     // ---------------- launches
     e->prof_cur.clear();
     size_t ev_next = 0;
-    auto launch = [&](const char* label, auto&& fn) -> hipError_t {
+    // events go on the stream the launch is enqueued on (a lane's, past the fork)
+    auto launch = [&](const char* label, hipStream_t ls, auto&& fn) -> hipError_t {
         if (!profiling || (!e->prof_only.empty() && e->prof_only != label)) return fn();
         while (e->ev_pool.size() < ev_next + 2) {
             hipEvent_t ev;
@@ -754,15 +755,15 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
             e->ev_pool.push_back(ev);
         }
         hipEvent_t a = e->ev_pool[ev_next++], b = e->ev_pool[ev_next++];
-        hipError_t st = hipEventRecord(a, s);
+        hipError_t st = hipEventRecord(a, ls);
         if (st == hipSuccess) st = fn();
-        if (st == hipSuccess) st = hipEventRecord(b, s);
+        if (st == hipSuccess) st = hipEventRecord(b, ls);
         e->prof_cur.push_back(Profile{label, a, b});
         return st;
     };
 #define QA_LAUNCH(label, expr)                                                              \
     do {                                                                                    \
-        hipError_t st_ = launch(label, [&]() { return (expr); });                          \
+        hipError_t st_ = launch(label, s, [&]() { return (expr); });                       \
         if (st_ != hipSuccess) {                                                            \
             set_err("%s: %s", label, hipGetErrorString(st_));                              \
             (void)hipGetLastError();                                                        \
@@ -777,17 +778,30 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     QA_LAUNCH("frontend", qa::frontend(s, pcm, d_clips, d_tiles, n_tiles, e->W<uint4>(e->basis), e->W<float>(e->melw),
                                        e->W<int>(e->melb0), logmel, key, flag));
     QA_LAUNCH("normalize", qa::normalize(s, logmel, d_clips, d_tiles, n_tiles, key));
-    // From the stem on, a large batch runs as two lanes: the tokens split at
-    // the attention window whose start is nearest the middle (a chunk
-    // boundary), and each half runs its stem chunks, conv_out, the layers and
+    // The first stem kernel (the fused conv1 + conv2, or conv1) over every chunk
+    if constexpr (std::is_same<T, qa::bf16>::value) {
+        if (fused_stem)
+            QA_LAUNCH("stem12", qa::stem12(s, logmel, d_chunks, n_chunks, e->W<uint4>(e->conv1_frag), e->W<T>(e->conv2_w),
+                                           e->W<float>(e->conv2_b), C, c2));
+        else
+            QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
+    } else {
+        QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
+    }
+    // From there on a large batch runs as two lanes: the tokens split at the
+    // attention window whose start is nearest the middle (a chunk boundary),
+    // and each half runs the rest of its stem chunks, conv_out, the layers and
     // the projection on a stream of its own (the caller's and the encoder's
     // second stream).  One half's tiles then fill the CUs that the other
     // half's last round of tiles leaves idle.  Rows (chunks, tokens) are
     // independent in every kernel and no window crosses the split, so the
-    // outputs are bit-identical to one lane's.  Not with taps or profiling
-    // (one lane: each kernel's time is its own), nor for the small batches
-    // that take split-K (one workspace for the partial sums).
-    const int lanes = (!taps && !profiling && n_tok > kSplitKMaxTokens && n_win >= 2) ? 2 : 1;
+    // outputs are bit-identical to one lane's.  Not with taps or with
+    // profiling of every launch (one lane: each kernel's time is its own; with
+    // profiling restricted to one label the lanes stay, and a launch in a lane
+    // is timed on that lane's stream), nor for the small batches that take
+    // split-K (one workspace for the partial sums).
+    const bool every_launch = profiling && e->prof_only.empty();
+    const int lanes = (!taps && !every_launch && n_tok > kSplitKMaxTokens && n_win >= 2) ? 2 : 1;
     int wsplit = n_win;
     if (lanes == 2) {
         wsplit = 1;
@@ -819,20 +833,8 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
             if (l == -2) {   // the lane's chunks: windows start at chunk boundaries
                 const int k0 = tok_src[t0] / qa::kChunkTok;
                 const int nk = (g + 1 < lanes ? tok_src[cu[gw[g + 1]]] / qa::kChunkTok : n_chunks) - k0;
-                const qa::ChunkInfo* dk = d_chunks + k0;
                 T* c1g = c1 + (size_t)k0 * 64 * 50 * C;
                 T* c2g = c2 + (size_t)k0 * 32 * 25 * C;
-                if constexpr (std::is_same<T, qa::bf16>::value) {
-                    if (fused_stem)
-                        QA_LAUNCH("stem12", qa::stem12(s, logmel, dk, nk, e->W<uint4>(e->conv1_frag), e->W<T>(e->conv2_w),
-                                                       e->W<float>(e->conv2_b), C, c2g));
-                    else
-                        QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, dk, nk, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b),
-                                                        C, c1g));
-                } else {
-                    QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, dk, nk, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C,
-                                                    c1g));
-                }
                 if (!fused_stem)   // NHWC conv1 output (VALU conv1)
                     QA_LAUNCH("conv2", qa::conv3x3s2<T>(s, c1g, nk, 64, 50, C, e->W<T>(e->conv2_w), e->W<float>(e->conv2_b),
                                                         c2g, false, lanes));

@@ -90,17 +90,22 @@ def kernel_work(d, lengths):
     return work, (ch, T, fr, wins)
 
 
-# Source files whose kernels the HBM-traffic figure in profiles/ was taken on.
+# Source files whose kernels the HBM-traffic figure in profiles/ was taken on:
+# the kernel's own file and the headers it includes (every source for a
+# kernel not listed).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "b17_20m_traffic.json")
 KERNEL_SOURCES = ["audio_encoder_front_amd/csrc/" + f for f in
                   ("gemm.hip", "stem.hip", "stem_fused.hip", "frontend.hip", "norm_attn.hip", "encoder.cpp", "qa_device.h",
                    "qa_kernels.h")]
+KERNEL_OWN_SOURCES = {
+    "stem12": ["audio_encoder_front_amd/csrc/" + f for f in ("stem_fused.hip", "qa_device.h", "qa_kernels.h")],
+}
 
 
-def sources_digest() -> str:
+def sources_digest(kernel: str = None) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_OWN_SOURCES.get(kernel, KERNEL_SOURCES):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -113,7 +118,7 @@ def measured_traffic(kernel: str, workload: str):
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("kernel") != kernel or rec.get("sources") != sources_digest():
+    if rec.get("workload") != workload or rec.get("kernel") != kernel or rec.get("sources") != sources_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 

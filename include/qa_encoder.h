@@ -199,8 +199,9 @@ int qa_encoder_enable_taps(qa_encoder *e, int enable);
 int64_t qa_encoder_tap(qa_encoder *e, int tap, float *dst, int64_t capacity);
 
 /* Per-kernel timing with HIP events recorded on the handle's stream around
- * every launch (0 disables; the default).  While it is on, every kernel runs
- * on the handle's stream alone, so that each time is that kernel's own.  qa_encoder_kernel_times fills up
+ * every launch (0 disables; the default).  While it times every launch, every
+ * kernel runs on the handle's stream alone, so that each time is that
+ * kernel's own (see qa_encoder_set_profiling_label for one label).  qa_encoder_kernel_times fills up
  * to `cap` entries of: a static NUL-terminated label, the summed
  * milliseconds and the launch count accumulated since profiling was last
  * enabled, and returns the number of labels (which may exceed cap). */
@@ -210,7 +211,11 @@ int qa_encoder_kernel_times(qa_encoder *e, const char **labels, double *total_ms
 
 /* Restrict the profiling events to the launches labelled `label` (a copy is
  * kept; NULL or "" = every launch, the default), so that a timed run carries
- * two events per such launch instead of two per kernel.  Returns
+ * two events per such launch instead of two per kernel.  Restricted, a batch
+ * of more than 4,096 tokens keeps its second stream (see
+ * qa_encoder_set_stream): the first stem kernel ("stem12" or "conv1") runs
+ * before the fork on the handle's stream, and a launch past the fork is timed
+ * on the stream it runs on, beside the other stream's work.  Returns
  * QA_STATUS_OK or INVALID_PARAMS (NULL handle). */
 int qa_encoder_set_profiling_label(qa_encoder *e, const char *label);
 
