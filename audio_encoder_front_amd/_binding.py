@@ -28,7 +28,7 @@ QA_TAP_LAYER0 = 2
 QA_NOALLOC_SCRATCH_BYTES = 160 * 1024 * 1024
 
 EXPORTS = ("qa_abi_version", "qa_last_error", "qa_encode_num_tokens", "qa_encoder_create",
-           "qa_encoder_set_stream", "qa_encode", "qa_encode_noalloc", "qa_encoder_enable_taps", "qa_encoder_tap",
+           "qa_encoder_set_stream", "qa_encoder_set_max_lanes", "qa_encode", "qa_encode_noalloc", "qa_encoder_enable_taps", "qa_encoder_tap",
            "qa_encoder_set_profiling", "qa_encoder_kernel_times", "qa_encoder_set_profiling_label",
            "qa_encoder_free", "qa_resample_length", "qa_resampler_create", "qa_resample", "qa_resampler_free",
            "qa_thinker_create", "qa_thinker_set_stream", "qa_thinker_prefill", "qa_thinker_free")
@@ -97,6 +97,8 @@ def _load() -> C.CDLL:
     lib.qa_encoder_tap.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int64]
     lib.qa_encoder_set_profiling.restype = C.c_int
     lib.qa_encoder_set_profiling.argtypes = [C.c_void_p, C.c_int]
+    lib.qa_encoder_set_max_lanes.restype = C.c_int
+    lib.qa_encoder_set_max_lanes.argtypes = [C.c_void_p, C.c_int]
     lib.qa_encoder_set_profiling_label.restype = C.c_int
     lib.qa_encoder_set_profiling_label.argtypes = [C.c_void_p, C.c_char_p]
     lib.qa_encoder_kernel_times.restype = C.c_int
@@ -270,6 +272,11 @@ def qa_encoder_tap(enc: Encoder, tap: int, dst) -> int:
 
 def qa_encoder_set_profiling(enc: Encoder, enable: bool) -> None:
     _check(_lib.qa_encoder_set_profiling(enc.handle, 1 if enable else 0))
+
+
+def qa_encoder_set_max_lanes(enc: Encoder, n: int) -> None:
+    """Streams an encode may run on: 1 (the handle's alone) or 2 (the default)."""
+    _check(_lib.qa_encoder_set_max_lanes(enc.handle, int(n)))
 
 
 def qa_encoder_set_profiling_label(enc: Encoder, label: Optional[str]) -> None:

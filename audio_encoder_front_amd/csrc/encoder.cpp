@@ -229,6 +229,7 @@ struct qa_encoder {
     hipStream_t stream = nullptr;
     int device = 0;
     // second lane of the layers (see run_encode): a stream and the fork/join events
+    int max_lanes = 2;
     hipStream_t lane = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // weights + constants in one device allocation
@@ -528,6 +529,13 @@ QA_API int qa_encoder_set_profiling(qa_encoder* e, int enable) {
     return QA_STATUS_OK;
 }
 
+QA_API int qa_encoder_set_max_lanes(qa_encoder* e, int n) {
+    if (!e) { set_err("encoder is NULL"); return QA_STATUS_INVALID_PARAMS; }
+    if (n != 1 && n != 2) { set_err("max lanes must be 1 or 2, got %d", n); return QA_STATUS_INVALID_PARAMS; }
+    e->max_lanes = n;
+    return QA_STATUS_OK;
+}
+
 QA_API int qa_encoder_set_profiling_label(qa_encoder* e, const char* label) {
     if (!e) { set_err("encoder is NULL"); return QA_STATUS_INVALID_PARAMS; }
     e->prof_only = label ? label : "";
@@ -801,7 +809,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     // is timed on that lane's stream), nor for the small batches that take
     // split-K (one workspace for the partial sums).
     const bool every_launch = profiling && e->prof_only.empty();
-    const int lanes = (!taps && !every_launch && n_tok > kSplitKMaxTokens && n_win >= 2) ? 2 : 1;
+    const int lanes = (e->max_lanes == 2 && !taps && !every_launch && n_tok > kSplitKMaxTokens && n_win >= 2) ? 2 : 1;
     int wsplit = n_win;
     if (lanes == 2) {
         wsplit = 1;

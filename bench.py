@@ -401,6 +401,9 @@ def main():
                     help="also time the layer GEMMs and conv2 through torch's vendor libraries (context)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for rocprofv3 byte counters)")
+    ap.add_argument("--lanes", type=int, default=2, choices=(1, 2),
+                    help="streams the timed workload may run on (qa_encoder_set_max_lanes; 1 for per-kernel "
+                         "profiles whose dispatches all cover the whole batch)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the encoder runs on a single MI355X and the library has no "
@@ -421,6 +424,7 @@ def main():
     enc = qa.qa_encoder_create(weights, wl.dims)
     stream = torch.cuda.current_stream(dev)
     qa.qa_encoder_set_stream(enc, stream)
+    qa.qa_encoder_set_max_lanes(enc, args.lanes)
     total_tok = sum(qa.qa_encode_num_tokens(n) for n in lengths)
     out = torch.empty((total_tok, wl.dims.output_dim), dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
@@ -501,7 +505,8 @@ def main():
         "dtype": wl.dims.dtype,
         "data": "synthetic (seeded speech-like PCM, N(0,0.02) bf16 weights)",
         "config": {"workload": f"{wl.name}: {wl.description}", "clips": len(lengths), "audio_s": audio_s,
-                   "tokens": T, "windows": len(wins), "chunks": n_chunks, "frames": n_frames},
+                   "tokens": T, "windows": len(wins), "chunks": n_chunks, "frames": n_frames,
+                   "max_streams": args.lanes},
         "tokens_per_s": round(T * args.steps / dt, 1),
         "mfma_util_pct": round(100.0 * total_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 2),
         "roofline": roof,

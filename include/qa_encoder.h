@@ -138,6 +138,14 @@ qa_encoder *qa_encoder_create(const qa_weights *w, const qa_dims *d);
  * QA_STATUS_OK or INVALID_PARAMS. */
 int qa_encoder_set_stream(qa_encoder *e, void *hip_stream);
 
+/* Streams a qa_encode call may run on: 1 keeps every launch on the handle's
+ * stream; 2 (the default) lets a batch of more than 4,096 tokens run half of
+ * its tokens, from conv3 on, on the handle's second stream (see
+ * qa_encoder_set_stream).  The results are bit-identical either way (rows are
+ * independent in every kernel and the split falls between attention windows).
+ * Returns QA_STATUS_OK, or INVALID_PARAMS for a NULL handle or n not 1 or 2. */
+int qa_encoder_set_max_lanes(qa_encoder *e, int n);
+
 /* Encode a packed batch: every step of the tower above, one packed forward
  * over all clips with one attention segment per window of every clip (M* ASR
  * page, Qwen3-ASR "Graph"; qwenasr.cpp "Windowed audio tower").

@@ -62,6 +62,7 @@ int main(void) {
     lens[0] = 32000; lens[1] = 0;
     CHECK(qa_encode(NULL, NULL, lens, 2, NULL) == QA_STATUS_INVALID_PARAMS);
     CHECK(qa_encoder_set_stream(NULL, NULL) == QA_STATUS_INVALID_PARAMS);
+    CHECK(qa_encoder_set_max_lanes(NULL, 1) == QA_STATUS_INVALID_PARAMS);
     CHECK(qa_encoder_enable_taps(NULL, 1) == QA_STATUS_INVALID_PARAMS);
     CHECK(qa_encoder_set_profiling(NULL, 1) == QA_STATUS_INVALID_PARAMS);
     CHECK(qa_encoder_tap(NULL, QA_TAP_LOG_MEL, NULL, 0) == -1);

@@ -104,6 +104,7 @@ def test_encode_rejects_bad_arguments_without_a_device(qa):
     lens = (ctypes.c_int64 * 2)(32000, 0)
     assert lib.qa_encode(None, None, lens, 2, None) == qa._binding.QA_STATUS_INVALID_PARAMS
     assert lib.qa_encoder_tap(None, 0, None, 0) == -1
+    assert lib.qa_encoder_set_max_lanes(None, 1) == qa._binding.QA_STATUS_INVALID_PARAMS
 
 
 def test_strict_c99_consumer(tmp_path, qa):

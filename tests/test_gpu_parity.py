@@ -175,9 +175,18 @@ def test_b06_packed_32_clips(b06):
     clips = synth.make_audio(wl32)
     _print("case: 0.6B bf16, 32 clips U(1,30) s")
     out, taps = run_gpu(enc, clips, taps=True)
-    # without taps the batch (5,986 tokens) runs as two lanes: bit-identical
+    # without taps the batch (5,986 tokens) runs as two lanes: bit-identical;
+    # and pinned to one stream (max lanes 1) without taps
+    import audio_encoder_front_amd as qa
     out2, _ = run_gpu(enc, clips)
     assert np.array_equal(out2, out)
+    qa.qa_encoder_set_max_lanes(enc, 1)
+    out1, _ = run_gpu(enc, clips)
+    qa.qa_encoder_set_max_lanes(enc, 2)
+    assert np.array_equal(out1, out)
+    for bad in (0, 3):
+        with pytest.raises(qa.QAError):
+            qa.qa_encoder_set_max_lanes(enc, bad)
     # every window of every clip (73), per window and per row, and the
     # log-mel of every clip
     rep = compare(wl.dims, w, clips, out, taps, progress="b06_32")
