@@ -7,17 +7,22 @@
 // "Front end and graph numerics": chunks padded independently).
 //
 // Tile: one chunk, 5 of conv2's 25 time columns x all 32 frequency rows (160
-// output pixels, row order (column, row) inside the tile) x 256 output
-// channels; 8 waves, each with all 160 pixels x 32 channels.  The K order is
-// conv2's (32-channel slab, tap, channel), so every 32-wide MFMA K block is one
-// (slab, tap).  Per slab the MFMAs read a conv1 patch from LDS: conv1's outputs
-// of the tile's receptive field for the slab's 32 channels (11 conv1 columns x
+// output pixels, row order (column, row) inside the tile) x every output
+// channel: 8 waves of 160 pixels x 64 channels (stems of more than 256
+// channels, up to 512) or x 32 channels (up to 256).  The K order is conv2's
+// (32-channel slab, tap, channel), so every 32-wide MFMA K block is one (slab,
+// tap).  Per slab the MFMAs read a conv1 patch from LDS: conv1's outputs of
+// the tile's receptive field for the slab's 32 channels (11 conv1 columns x
 // 65 conv1 rows, -1 .. 63; row -1 and column -1 are conv2's zero padding),
-// computed by a split-input MFMA (below) and the GELU.  The
-// patch is double-buffered: while the waves multiply slab s they compute slab
-// s + 1's patch into the other buffer (one barrier per slab).  A wave's 32
-// weight rows are its own, so they go global -> registers, three taps ahead,
-// with no LDS and no barrier.
+// computed by a split-input MFMA (below) and the GELU, once per pixel tile
+// for all output channels.  The patch is double-buffered: while the waves
+// multiply slab s they compute slab s + 1's patch into the other buffer (one
+// barrier per slab).  With 32 channels per wave a wave interleaves its patch
+// groups with its MFMAs; with 64 (160 accumulator registers) waves 0-3 compute
+// theirs before their MFMAs and waves 4-7 after, so that the two waves of a
+// SIMD (w and w + 4) overlap one's VALU work with the other's MFMAs.  A wave's
+// weight rows are its own, so they go global -> registers (buffer loads),
+// three taps ahead (one with 64 channels), with no LDS and no barrier.
 //
 // conv1 on MFMA: K = 9 taps x 3 bf16 parts (hi + mid + lo, which add up to
 // the fp32 log-mel value to within one fp32 ulp) + 1 bias slot = 28 <= 32, so
@@ -29,10 +34,13 @@
 // wider than 512 channels), and the output was checked bit-identical to that
 // route when both existed.
 //
-// LDS: two patches (46,464 B each), the tile's log-mel window (11,868 B) and
-// the conv1 B operands of every wave's pixel groups (49,152 B; the same for
-// every slab, built once, kept out of the registers).  The first two
-// fragments of the next tap are read during the current tap's MFMAs.
+// LDS: two patches (46,464 B each), the tile's log-mel window (11,868 B), the
+// conv1 B operands of every wave's pixel groups (49,152 B; the same for every
+// slab, built once, kept out of the registers) and two slabs' conv1 A
+// fragments (4,096 B, loaded global -> LDS directly, slab s + 2's during slab
+// s).  With 32 channels per wave the first two fragments of the next tap are
+// read during the current tap's MFMAs; with 64 the slab's 90 (tap, fragment)
+// reads run two fragments ahead of their MFMAs.
 // Patch layout: [conv1 column 11][row parity 2][row / 2 33][32 channels]: a
 // conv2 tap reads the conv1 rows 2 i + a of 16 consecutive output rows i,
 // which this layout keeps 64 bytes apart; the 16-byte channel chunks are
@@ -61,11 +69,15 @@ constexpr int kFsMelT = 4 * kFsCols + 3;                // 23 frames
 constexpr int kFsMelBytes = kFsMelRows * kFsMelT * 4;   // 11,868
 constexpr int kFsOffMel = 2 * kFsPatchBytes;
 constexpr int kFsOffBop = (kFsOffMel + kFsMelBytes + 15) / 16 * 16;
-constexpr int kFsLds = kFsOffBop + 8 * kFsGpw * 64 * 16;   // + the conv1 B operands: 153,952 B
+constexpr int kFsOffWa = kFsOffBop + 8 * kFsGpw * 64 * 16;   // + the conv1 B operands
+constexpr int kFsLds = kFsOffWa + 2 * 2048;             // + two slabs' conv1 A fragments: 158,048 B
 constexpr int kFsPrefetch = 2;                          // fragments of the next tap read ahead
-constexpr int kFsWAhead = 3;                            // weight taps in flight per wave
+constexpr int kFsWAhead = 3;                            // weight taps in flight per wave (256-channel tiles)
+constexpr int kFsWAheadWide = 1;                        // (512-channel tiles: 64 channels per wave)
+constexpr int kFsStream = 2;                            // patch fragments read ahead (512-channel tiles)
 static_assert(kFsM * 256 * 2 <= 2 * kFsPatchBytes, "epilogue staging fits the patches");
-static_assert(9 % kFsWAhead == 0, "the weight ring position of a tap is the same in every slab");
+static_assert(9 % kFsWAhead == 0 && 9 % kFsWAheadWide == 0,
+              "the weight ring position of a tap is the same in every slab");
 
 __device__ __forceinline__ int fs_patch_off(int pcol, int prow, int chunk) {
     const int par = prow & 1, ri = prow >> 1;
@@ -73,7 +85,11 @@ __device__ __forceinline__ int fs_patch_off(int pcol, int prow, int chunk) {
 }
 constexpr int kFsDummy = (1 * kFsRi + 32) * 64;         // column 0, parity 1, row / 2 32: never read
 
-template <int NCB>   // 32-channel slabs of conv1's output = conv2's input (C = 32 NCB)
+// NCB: 32-channel slabs of conv1's output = conv2's input (C = 32 NCB).
+// NJ: 16-channel fragments per wave, 2 (a workgroup covers 256 output
+// channels) or 4 (512: every channel of the stem, so each slab's conv1 patch
+// is computed once per pixel tile instead of once per 256-channel half).
+template <int NCB, int NJ>
 __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ logmel,
                                                      const ChunkInfo* __restrict__ chunks,
                                                      const uint4* __restrict__ wfrag,
@@ -81,6 +97,8 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
                                                      const float* __restrict__ b2,
                                                      bf16* __restrict__ out) {
     constexpr int C = 32 * NCB, K = 9 * C, NT = 9 * NCB;   // NT: (slab, tap) K blocks
+    constexpr int WN = 16 * NJ, BN = 8 * WN;              // output channels per wave / per workgroup
+    constexpr int WAH = NJ == 2 ? kFsWAhead : kFsWAheadWide;
     __shared__ __align__(1024) char smem[kFsLds];
     float* img = reinterpret_cast<float*>(smem + kFsOffMel);
 
@@ -88,23 +106,36 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int fr = lane & 15, fg = lane >> 4;
     const int chunk = blockIdx.x / kFsTilesPerChunk, j0 = (blockIdx.x % kFsTilesPerChunk) * kFsCols;
-    const int n0 = blockIdx.y * 256 + wave * 32;          // this wave's first output channel
+    const int n0 = blockIdx.y * BN + wave * WN;           // this wave's first output channel
     const ChunkInfo ci = chunks[chunk];
 
     // ---- this wave's weight rows n0 + 16 j + fr (rows past C repeat row C - 1:
     // their outputs are never stored); K block t = (slab, tap) at element 32 t
-    const bf16* wrow[2];
+    // (buffer loads: one 32-bit byte offset per row instead of a 64-bit address)
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)w2, (short)0, C * K * 2, 0x00020000);
+    int wrow[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wrow[j] = w2 + (size_t)min(n0 + 16 * j + fr, C - 1) * K + 8 * fg;
-    uint4 wb[kFsWAhead][2];
+    for (int j = 0; j < NJ; ++j) wrow[j] = (min(n0 + 16 * j + fr, C - 1) * K + 8 * fg) * 2;
+    uint4 wb[WAH][NJ];
     auto load_w = [&](int t, uint4* dst) {
         const int tc = min(t, NT - 1);                   // past the last block: a repeat, unused
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dst[j] = ld16(wrow[j] + 32 * tc);
+        for (int j = 0; j < NJ; ++j)
+            dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, wrow[j] + 64 * tc, 0, 0));
     };
 #pragma unroll
-    for (int r = 0; r < kFsWAhead; ++r) load_w(r, wb[r]);
-    const uint4 wa00 = wfrag[lane], wa01 = wfrag[64 + lane];   // conv1 fragments of slab 0
+    for (int r = 0; r < WAH; ++r) load_w(r, wb[r]);
+    // conv1's A fragments (2 x 64 lanes x 16 B per slab, the same for every
+    // wave) go global -> LDS, slab s's into buffer s & 1: slabs 0 and 1 now,
+    // slab s + 2 during slab s (after slab s - 1 has read that buffer)
+    char* wab = smem + kFsOffWa;
+    const unsigned wab_lds = (unsigned)(uintptr_t)(lds_void*)wab;
+    auto load_wa = [&](int slab_idx) {   // by waves 0 and 1
+        if (wave < 2) dma16(wfrag + (size_t)(2 * slab_idx + wave) * 64 + lane, wab_lds + (slab_idx & 1) * 2048 + wave * 1024);
+    };
+    load_wa(0);
+    if (NCB > 1 && wave >= 2 && wave < 4)
+        dma16(wfrag + (size_t)(2 + wave - 2) * 64 + lane, wab_lds + 2048 + (wave - 2) * 1024);
 
     // ---- the tile's log-mel window: rows -1 .. 127, frames 4 j0 - 3 .. 4 j0 + 19
     // (zeros outside the chunk's frames), [frame][row]
@@ -126,18 +157,8 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
             if (tid + 512 * k < kFsMelRows * kFsMelT) img[tid + 512 * k] = v[k];
     }
 
-    // ---- accumulators, bias as the start value: lane holds out[m = fr][n = 4 fg + r]
-    f32x4 acc[10][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = n0 + j * 16 + 4 * fg;
-        f32x4 b = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) b[r] = n + r < C ? b2[n + r] : 0.f;
-#pragma unroll
-        for (int f = 0; f < 10; ++f) acc[f][j] = b;
-    }
-    __syncthreads();                                     // the mel window is in LDS
+    __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this wave's conv1 fragment loads
+    __syncthreads();                                     // the mel window and the fragments are in LDS
 
     // ---- conv1 B operands of this wave's pixel groups (the same for every
     // slab): lane (px, g) holds K entries 8 g .. 8 g + 7 of pixel px: tap k / 3
@@ -145,15 +166,19 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
     // the constant 1 of the bias slot.  Each group's LDS destination in the
     // patch (the dummy slot for pixels past it) and its padding flag.
     uint4* bop_lds = reinterpret_cast<uint4*>(smem + kFsOffBop) + wave * kFsGpw * 64 + lane;
-    int pdst[kFsGpw];
-    bool ppad[kFsGpw];
+    // group u's pixel, its patch destination (the dummy slot past the patch)
+    // and whether it is conv2's zero padding (recomputed per use: registers)
+    auto gpix = [&](int u, int& pc, int& pr, int frx) {
+        const int p = (wave + 8 * u) * 16 + frx;
+        const bool in = p < kFsPix;
+        pc = in ? p / kFsProw : 0;
+        pr = in ? p - pc * kFsProw : 1;
+        return in;
+    };
 #pragma unroll
     for (int u = 0; u < kFsGpw; ++u) {
-        const int p = (wave + 8 * u) * 16 + fr;
-        const bool in = p < kFsPix;
-        const int pc = in ? p / kFsProw : 0, pr = in ? p - pc * kFsProw : 1;
-        pdst[u] = in ? fs_patch_off(pc, pr, fg) : kFsDummy + (fg << 4);
-        ppad[u] = pr == 0 || (pc == 0 && j0 == 0);
+        int pc, pr;
+        gpix(u, pc, pr, fr);
         const int base = 2 * pc * kFsMelRows + 2 * max(pr, 1) - 2;   // rows past the top are padding
         bf16 bv[8];
 #pragma unroll
@@ -170,8 +195,12 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
         const bf16x8 b8 = {bv[0], bv[1], bv[2], bv[3], bv[4], bv[5], bv[6], bv[7]};
         bop_lds[u * 64] = __builtin_bit_cast(uint4, b8);
     }
-    // one pixel group of slab s's patch into buffer pb
-    auto conv1_group = [&](int u, const uint4& wa0, const uint4& wa1, char* pb) {
+    // one pixel group of slab s's patch into buffer pb.  The group's pixel is
+    // derived from an opaque copy of the lane id, so that the compiler
+    // recomputes it (a few integer operations) instead of keeping every
+    // group's destination in registers through the slab loop.
+    auto conv1_group = [&](int u, const char* wa, char* pb) {
+        const uint4 wa0 = ld16(wa + lane * 16), wa1 = ld16(wa + 1024 + lane * 16);
         const uint4 bu = bop_lds[u * 64];
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa0),
@@ -181,91 +210,170 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
         const bf16x8 o = {(bf16)gelu_erf_bf16(a0[0]), (bf16)gelu_erf_bf16(a0[1]), (bf16)gelu_erf_bf16(a0[2]),
                           (bf16)gelu_erf_bf16(a0[3]), (bf16)gelu_erf_bf16(a1[0]), (bf16)gelu_erf_bf16(a1[1]),
                           (bf16)gelu_erf_bf16(a1[2]), (bf16)gelu_erf_bf16(a1[3])};
-        *reinterpret_cast<uint4*>(pb + pdst[u]) = ppad[u] ? make_uint4(0u, 0u, 0u, 0u) : __builtin_bit_cast(uint4, o);
+        int frx = fr, pc, pr;
+        asm volatile("" : "+v"(frx));
+        const bool in = gpix(u, pc, pr, frx);
+        const int dst = in ? fs_patch_off(pc, pr, fg) : kFsDummy + (fg << 4);
+        const bool pad = pr == 0 || (pc == 0 && j0 == 0);
+        *reinterpret_cast<uint4*>(pb + dst) = pad ? make_uint4(0u, 0u, 0u, 0u) : __builtin_bit_cast(uint4, o);
     };
 #pragma unroll
-    for (int u = 0; u < kFsGpw; ++u) conv1_group(u, wa00, wa01, smem);
+    for (int u = 0; u < kFsGpw; ++u) conv1_group(u, wab, smem);
     __syncthreads();                                     // slab 0's patch
 
+    // ---- accumulators, bias as the start value: lane holds out[m = fr][n = 4 fg + r]
+    // (set up after the first patch, whose registers are free by then)
+    f32x4 acc[10][NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + j * 16 + 4 * fg;
+        f32x4 b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[r] = n + r < C ? b2[n + r] : 0.f;
+#pragma unroll
+        for (int f = 0; f < 10; ++f) acc[f][j] = b;
+    }
+    const int fbase0 = fr * 64 + ((fg ^ ((fr >> 1) & 3)) << 4);
+    const int fbase1 = fr * 64 + ((fg ^ (((fr + 1) >> 1) & 3)) << 4);
     // one slab: 9 taps of 20 MFMAs from patch buffer s & 1; with NEXT, slab
     // s + 1's patch into the other buffer, one pixel group every 1.5 taps
     auto slab = [&](int s, auto next_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
         const char* pa = smem + (s & 1) * kFsPatchBytes;
         char* pn = smem + ((s + 1) & 1) * kFsPatchBytes;
-        uint4 wa0, wa1;
+        const char* wan = wab + ((s + 1) & 1) * 2048;     // slab s + 1's conv1 fragments
         if constexpr (NEXT) {
-            wa0 = wfrag[(size_t)(2 * s + 2) * 64 + lane];
-            wa1 = wfrag[(size_t)(2 * s + 3) * 64 + lane];
+            if (s + 2 < NCB) load_wa(s + 2);
         }
+        // fragment f of tap (a, b): conv1 rows 2 i + a, i = 16 (f & 1) + fr, of
+        // column 2 (f >> 1) + b, i.e. patch row ri = fr + 16 (f & 1) + a / 2 of
+        // parity a & 1.  The swizzle ((ri >> 1) & 3) then depends on the lane
+        // and on a / 2 only, so every read is one of two per-lane bases plus a
+        // constant offset (the 90 reads of a slab need no address registers).
         auto read_frag = [&](int tap, int f) {
-            const int a = tap / 3, bb = tap - 3 * a, jj = f >> 1, i = (f & 1) * 16 + fr;
-            return ld16(pa + fs_patch_off(2 * jj + bb, 2 * i + a, fg));
+            const int a = tap / 3, bb = tap - 3 * a, pcol = 2 * (f >> 1) + bb;
+            const int cofs = ((pcol * 2 + (a & 1)) * kFsRi + 16 * (f & 1) + (a >> 1)) * 64;
+            return ld16(pa + ((a >> 1) ? fbase1 : fbase0) + cofs);
         };
-        uint4 fn[kFsPrefetch];
+        if constexpr (NJ == 2) {
+            uint4 fn[kFsPrefetch];
 #pragma unroll
-        for (int f = 0; f < kFsPrefetch; ++f) fn[f] = read_frag(0, f);
+            for (int f = 0; f < kFsPrefetch; ++f) fn[f] = read_frag(0, f);
 #pragma unroll
-        for (int tap = 0; tap < 9; ++tap) {
-            const uint4 fb0 = wb[tap % kFsWAhead][0], fb1 = wb[tap % kFsWAhead][1];
-            load_w(9 * s + tap + kFsWAhead, wb[tap % kFsWAhead]);
-            uint4 fa[10];
+            for (int tap = 0; tap < 9; ++tap) {
+                const uint4 fb0 = wb[tap % WAH][0], fb1 = wb[tap % WAH][1];
+                load_w(9 * s + tap + WAH, wb[tap % WAH]);
+                uint4 fa[10];
 #pragma unroll
-            for (int f = 0; f < kFsPrefetch; ++f) fa[f] = fn[f];
+                for (int f = 0; f < kFsPrefetch; ++f) fa[f] = fn[f];
 #pragma unroll
-            for (int f = kFsPrefetch; f < 10; ++f) fa[f] = read_frag(tap, f);
-            if (tap + 1 < 9) {
+                for (int f = kFsPrefetch; f < 10; ++f) fa[f] = read_frag(tap, f);
+                if (tap + 1 < 9) {
 #pragma unroll
-                for (int f = 0; f < kFsPrefetch; ++f) fn[f] = read_frag(tap + 1, f);
+                    for (int f = 0; f < kFsPrefetch; ++f) fn[f] = read_frag(tap + 1, f);
+                }
+#pragma unroll
+                for (int f = 0; f < 10; ++f) mfma_kblock(bf16(), fb0, fa[f], acc[f][0]);
+#pragma unroll
+                for (int f = 0; f < 10; ++f) mfma_kblock(bf16(), fb1, fa[f], acc[f][1]);
+                if constexpr (NEXT) {
+                    if (tap % 3 != 2) conv1_group(2 * (tap / 3) + tap % 3, wan, pn);
+                }
             }
+        } else {
+            // 64 channels per wave: each patch fragment feeds NJ MFMAs, read
+            // kFsStream fragments ahead through the slab's 90 (tap, fragment)
+            // steps.  The next slab's patch work is not interleaved (its
+            // registers would not fit beside 160 accumulators): waves 0-3 do
+            // their pixel groups before their MFMAs, waves 4-7 after theirs,
+            // so on every SIMD (waves w and w + 4) one wave runs the VALU work
+            // while the other keeps the matrix core busy.
+            auto conv1_phase = [&]() {
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int f = 0; f < 10; ++f) mfma_kblock(bf16(), fb0, fa[f], acc[f][0]);
-#pragma unroll
-            for (int f = 0; f < 10; ++f) mfma_kblock(bf16(), fb1, fa[f], acc[f][1]);
+                for (int u = 0; u < kFsGpw; ++u) conv1_group(u, wan, pn);
+                __builtin_amdgcn_sched_barrier(0);
+            };
             if constexpr (NEXT) {
-                if (tap % 3 != 2) conv1_group(2 * (tap / 3) + tap % 3, wa0, wa1, pn);
+                if (wave < 4) conv1_phase();
+            }
+            uint4 ring[kFsStream];
+#pragma unroll
+            for (int q = 0; q < kFsStream; ++q) ring[q] = read_frag(q / 10, q % 10);
+#pragma unroll
+            for (int tap = 0; tap < 9; ++tap) {
+                uint4 fb[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) fb[j] = wb[tap % WAH][j];
+                load_w(9 * s + tap + WAH, wb[tap % WAH]);
+#pragma unroll
+                for (int f = 0; f < 10; ++f) {
+                    const int q = tap * 10 + f;
+                    const uint4 fa = ring[q % kFsStream];
+                    if (q + kFsStream < 90) ring[q % kFsStream] = read_frag((q + kFsStream) / 10, (q + kFsStream) % 10);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) mfma_kblock(bf16(), fb[j], fa, acc[f][j]);
+                    __builtin_amdgcn_sched_barrier(0);   // keeps the register ring from being hoisted
+                }
+            }
+            if constexpr (NEXT) {
+                if (wave >= 4) conv1_phase();
             }
         }
+        if constexpr (NEXT) __builtin_amdgcn_s_waitcnt(0x0F70);   // slab s + 2's conv1 fragments landed
         __syncthreads();   // reads of buffer s & 1 done; slab s + 1's patch complete
     };
     for (int s = 0; s + 1 < NCB; ++s) slab(s, std::true_type{});
     slab(NCB - 1, std::false_type{});
 
     // ---- epilogue: GELU, bf16, staged row-major through the patch buffers
-    // (rows of 512 B, 16-byte chunks XOR-swizzled by row % 16), then whole
-    // 16-byte chunks of output rows: pixel (column jj, row i) of the tile is
-    // row (chunk, i, j0 + jj) of conv2's NHWC output
-#pragma unroll
-    for (int f = 0; f < 10; ++f) {
-        const int m = f * 16 + fr;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = wave * 32 + j * 16 + 4 * fg;  // 4 channels = half of chunk n / 8
-            const int c16 = (n >> 3) ^ (m & 15);
-            store4(reinterpret_cast<bf16*>(smem + m * 512 + (c16 << 4) + ((n & 4) << 1)),
-                   gelu_erf_bf16(acc[f][j][0]), gelu_erf_bf16(acc[f][j][1]), gelu_erf_bf16(acc[f][j][2]),
-                   gelu_erf_bf16(acc[f][j][3]));
-        }
-    }
-    __syncthreads();
+    // (rows of 256 channels = 512 B, 16-byte chunks XOR-swizzled by row % 16),
+    // then whole 16-byte chunks of output rows: pixel (column jj, row i) of the
+    // tile is row (chunk, i, j0 + jj) of conv2's NHWC output.  A 512-channel
+    // tile goes out in two passes of 256 channels (waves 0-3, then 4-7).
     bf16* obase = out + (size_t)chunk * 800 * C;
-    const int nt0 = blockIdx.y * 256;
-    for (int idx = tid; idx < kFsM * 32; idx += 512) {
-        const int m = idx >> 5, c = idx & 31;
-        const int n = nt0 + 8 * c;
-        if (n >= C) continue;
-        const int jj = m >> 5, i = m & 31;
-        const uint4 v = ld16(smem + m * 512 + ((c ^ (m & 15)) << 4));
-        *reinterpret_cast<uint4*>(obase + ((size_t)i * 25 + j0 + jj) * C + n) = v;
+    constexpr int PASSES = BN / 256;
+#pragma unroll
+    for (int h = 0; h < PASSES; ++h) {
+        if (h > 0) __syncthreads();                      // the previous pass's rows are out
+        if (PASSES == 1 || (wave >> 2) == h) {
+#pragma unroll
+            for (int f = 0; f < 10; ++f) {
+                const int m = f * 16 + fr;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int n = (wave * WN) % 256 + j * 16 + 4 * fg;   // 4 channels = half of chunk n / 8
+                    const int c16 = (n >> 3) ^ (m & 15);
+                    store4(reinterpret_cast<bf16*>(smem + m * 512 + (c16 << 4) + ((n & 4) << 1)),
+                           gelu_erf_bf16(acc[f][j][0]), gelu_erf_bf16(acc[f][j][1]), gelu_erf_bf16(acc[f][j][2]),
+                           gelu_erf_bf16(acc[f][j][3]));
+                }
+            }
+        }
+        __syncthreads();
+        const int nt0 = blockIdx.y * BN + h * 256;
+        for (int idx = tid; idx < kFsM * 32; idx += 512) {
+            const int m = idx >> 5, c = idx & 31;
+            const int n = nt0 + 8 * c;
+            if (n >= C) continue;
+            const int jj = m >> 5, i = m & 31;
+            const uint4 v = ld16(smem + m * 512 + ((c ^ (m & 15)) << 4));
+            *reinterpret_cast<uint4*>(obase + ((size_t)i * 25 + j0 + jj) * C + n) = v;
+        }
     }
 }
 
 hipError_t stem12(hipStream_t s, const float* logmel, const ChunkInfo* chunks, int n_chunks, const uint4* wfrag,
                   const bf16* w2, const float* b2, int C, bf16* out) {
     if (n_chunks <= 0) return hipSuccess;
-    const dim3 grid((unsigned)(n_chunks * kFsTilesPerChunk), (unsigned)((C + 255) / 256));
+    // one workgroup per pixel tile: 256 channels (8 waves of 32) for stems of
+    // up to 256 channels, 512 (8 waves of 64) above
+    const dim3 grid((unsigned)(n_chunks * kFsTilesPerChunk));
     switch (C) {   // C is a multiple of 32, at most 512 (the MFMA conv1's limit)
-#define QA_S12(ncb) case 32 * ncb: stem12_kernel<ncb><<<grid, 512, 0, s>>>(logmel, chunks, wfrag, w2, b2, out); break;
+#define QA_S12(ncb)                                                                                       \
+    case 32 * ncb:                                                                                        \
+        stem12_kernel<ncb, (ncb > 8 ? 4 : 2)><<<grid, 512, 0, s>>>(logmel, chunks, wfrag, w2, b2, out);   \
+        break;
         QA_S12(1) QA_S12(2) QA_S12(3) QA_S12(4) QA_S12(5) QA_S12(6) QA_S12(7) QA_S12(8)
         QA_S12(9) QA_S12(10) QA_S12(11) QA_S12(12) QA_S12(13) QA_S12(14) QA_S12(15) QA_S12(16)
 #undef QA_S12
