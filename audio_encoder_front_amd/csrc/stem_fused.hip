@@ -331,6 +331,16 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
     // then whole 16-byte chunks of output rows: pixel (column jj, row i) of the
     // tile is row (chunk, i, j0 + jj) of conv2's NHWC output.  A 512-channel
     // tile goes out in two passes of 256 channels (waves 0-3, then 4-7).
+    // (every wave converts its outputs first, so that the GELUs of both passes
+    // run on all SIMDs at once)
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 ov[10][NJ];
+#pragma unroll
+    for (int f = 0; f < 10; ++f)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            ov[f][j] = bf16x4{(bf16)gelu_erf_bf16(acc[f][j][0]), (bf16)gelu_erf_bf16(acc[f][j][1]),
+                              (bf16)gelu_erf_bf16(acc[f][j][2]), (bf16)gelu_erf_bf16(acc[f][j][3])};
     bf16* obase = out + (size_t)chunk * 800 * C;
     constexpr int PASSES = BN / 256;
 #pragma unroll
@@ -344,9 +354,7 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
                 for (int j = 0; j < NJ; ++j) {
                     const int n = (wave * WN) % 256 + j * 16 + 4 * fg;   // 4 channels = half of chunk n / 8
                     const int c16 = (n >> 3) ^ (m & 15);
-                    store4(reinterpret_cast<bf16*>(smem + m * 512 + (c16 << 4) + ((n & 4) << 1)),
-                           gelu_erf_bf16(acc[f][j][0]), gelu_erf_bf16(acc[f][j][1]), gelu_erf_bf16(acc[f][j][2]),
-                           gelu_erf_bf16(acc[f][j][3]));
+                    *reinterpret_cast<bf16x4*>(smem + m * 512 + (c16 << 4) + ((n & 4) << 1)) = ov[f][j];
                 }
             }
         }
