@@ -810,8 +810,18 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     // split-K (one workspace for the partial sums).
     const bool every_launch = profiling && e->prof_only.empty();
     const int lanes = (e->max_lanes == 2 && !taps && !every_launch && n_tok > kSplitKMaxTokens && n_win >= 2) ? 2 : 1;
+    // If a launch fails after the fork, the call returns early: wait for what
+    // the second stream already holds, so that no work of this call outlives it
+    // (the next call may grow, and so free, the workspace).
+    struct LaneGuard {
+        hipStream_t lane = nullptr;
+        ~LaneGuard() {
+            if (lane) (void)hipStreamSynchronize(lane);
+        }
+    } lane_guard;
     int wsplit = n_win;
     if (lanes == 2) {
+        lane_guard.lane = e->lane;
         wsplit = 1;
         for (int w = 2; w < n_win; ++w)
             if (std::abs(2 * (int64_t)cu[w] - n_tok) < std::abs(2 * (int64_t)cu[wsplit] - n_tok)) wsplit = w;
@@ -901,6 +911,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     if (lanes == 2) {
         QA_LAUNCH("join", hipEventRecord(e->ev_join, e->lane));
         QA_LAUNCH("join", hipStreamWaitEvent(s, e->ev_join, 0));
+        lane_guard.lane = nullptr;   // the caller's stream now waits for the second one
     }
     QA_LAUNCH("flag", hipMemcpyAsync(e->flag_host, flag, sizeof(int), hipMemcpyDeviceToHost, s));
 #undef QA_LAUNCH
