@@ -618,6 +618,13 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     std::vector<qa::FrontTile> tiles;
     std::vector<qa::ChunkInfo> chunks;
     std::vector<int> tok_src, cu{0};
+    {   // capacities from the frame counts (one pass over the lengths)
+        int64_t frames = 0;
+        for (int i = 0; i < n_clips; ++i) frames += lengths[i] / kHop;
+        tiles.reserve((size_t)(frames / qa::kFrontFrames + 2 * n_clips));
+        chunks.reserve((size_t)(frames / qa::kChunk + n_clips));
+        tok_src.reserve((size_t)((frames / qa::kChunk + n_clips) * qa::kChunkTok));
+    }
     int64_t sample_off = 0;
     int64_t frame_row = 0;
     // window_chunks == 0: one attention segment per clip (full-input attention)
@@ -637,7 +644,8 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
             const int m = std::min(qa::kChunk, nf - c0);
             const int ch = (int)chunks.size();
             chunks.push_back(qa::ChunkInfo{(int32_t)(frame_row + c0), m});
-            for (int j = 0; j < after_cnn(m); ++j) tok_src.push_back(ch * qa::kChunkTok + j);
+            const int nt = after_cnn(m);
+            for (int j = 0; j < nt; ++j) tok_src.push_back(ch * qa::kChunkTok + j);
         }
         const int ntok = (int)tok_src.size() - tok0;
         for (int s = 0; s < ntok; s += win_tok) cu.push_back(tok0 + std::min(s + win_tok, ntok));
