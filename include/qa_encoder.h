@@ -162,8 +162,10 @@ int qa_encoder_set_max_lanes(qa_encoder *e, int n);
  *            x output_dim], rows clip-major, then chunk, then token-in-chunk.
  *            Caller-owned; may be NULL when the total is 0.
  * All argument checks happen before any device work.  The work is enqueued
- * on the handle's stream; the call then synchronises that stream to read a
- * device-side validation flag.  Returns QA_STATUS_OK; INVALID_PARAMS for bad
+ * on the handle's stream (a batch of more than 4,096 tokens also on the
+ * handle's second stream, joined back into it: see qa_encoder_set_stream);
+ * the call then synchronises the handle's stream to read a device-side
+ * validation flag.  Returns QA_STATUS_OK; INVALID_PARAMS for bad
  * arguments, a nonfinite sample (any sample of any clip) or a power or mel
  * value beyond float32 range in any STFT frame, the dropped final frame
  * included (OneSpeech "Low-level recognition": such inputs are rejected;
