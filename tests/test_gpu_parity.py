@@ -187,6 +187,16 @@ def test_b06_packed_32_clips(b06):
     for bad in (0, 3):
         with pytest.raises(qa.QAError):
             qa.qa_encoder_set_max_lanes(enc, bad)
+    # the bench's timed steps: events around the fused stem only, lanes kept
+    # (the stem runs once per encode, before the fork)
+    qa.qa_encoder_set_profiling_label(enc, "stem12")
+    qa.qa_encoder_set_profiling(enc, True)
+    outp, _ = run_gpu(enc, clips)
+    times = qa.qa_encoder_kernel_times(enc)
+    qa.qa_encoder_set_profiling(enc, False)
+    qa.qa_encoder_set_profiling_label(enc, None)
+    assert np.array_equal(outp, out)
+    assert set(times) == {"stem12"} and times["stem12"][1] == 1 and times["stem12"][0] > 0
     # every window of every clip (73), per window and per row, and the
     # log-mel of every clip
     rep = compare(wl.dims, w, clips, out, taps, progress="b06_32")
