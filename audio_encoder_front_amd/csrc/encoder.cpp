@@ -675,7 +675,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     // ---------------- workspace
     const size_t o_logmel = slot((size_t)n_frames * qa::kMels * 4);
     const size_t o_key = slot((size_t)n_clips * 4);
-    const size_t o_flag = slot(4);
+    const size_t o_flag = slot(8);                 // the nonfinite-input flag, the fused stem's tile counter
     // bf16 with the MFMA conv1: conv1 and conv2 run as one kernel and conv1's
     // output is never stored
     const bool fused_stem = std::is_same<T, qa::bf16>::value && e->conv1_frag != 0;
@@ -798,7 +798,7 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     if constexpr (std::is_same<T, qa::bf16>::value) {
         if (fused_stem)
             QA_LAUNCH("stem12", qa::stem12(s, logmel, d_chunks, n_chunks, e->W<uint4>(e->conv1_frag), e->W<T>(e->conv2_w),
-                                           e->W<float>(e->conv2_b), C, c2));
+                                           e->W<float>(e->conv2_b), C, c2, flag + 1));
         else
             QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
     } else {

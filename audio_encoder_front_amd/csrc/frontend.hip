@@ -45,7 +45,10 @@ __device__ __forceinline__ int pad_index(int s) { return s + 8 * (s / 160); }
 __global__ void init_flags_kernel(int* clip_key, int n_clips, int* flag) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n_clips) clip_key[i] = float_key(-INFINITY);
-    if (i == 0) *flag = 0;
+    if (i == 0) {
+        flag[0] = 0;
+        flag[1] = 0;   // the fused stem's tile counter
+    }
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void frontend_kernel(

@@ -135,6 +135,11 @@ __device__ __forceinline__ void dma16_buf(i32x4 rsrc, unsigned voff, unsigned ld
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff),
                  "s"(rsrc) : "m0");
 }
+// One dword per lane: the wave's 64 dwords land at lds_addr + 4 * lane.
+__device__ __forceinline__ void dma4_buf(i32x4 rsrc, unsigned voff, unsigned lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff),
+                 "s"(rsrc) : "m0");
+}
 // Raw buffer resource (stride 0) over [base, base + bytes), bytes clamped
 // below kOobOffset; the fourth word is the gfx9 raw-buffer format.
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint64_t bytes) {

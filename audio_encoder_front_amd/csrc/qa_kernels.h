@@ -46,6 +46,8 @@ constexpr int kConvCB = 32;          // input-channel block of the conv2/conv3 K
 void set_error_message(const char* msg);
 
 // ---- front end
+// clip_key[i] = the key of -inf (per-clip maxima start there); flag[0] = 0
+// (the nonfinite-input flag) and flag[1] = 0 (the fused stem's tile counter).
 hipError_t init_flags(hipStream_t s, int* clip_key, int n_clips, int* flag);
 // basis: the Hann-windowed cos / sin DFT basis as bf16 MFMA A fragments, each
 // fp32 value split exactly into hi + mid + lo: [13 bin chunks][13 K blocks of
@@ -72,8 +74,10 @@ hipError_t conv1(hipStream_t s, const float* logmel, const ChunkInfo* chunks, in
 // K slot 27) and conv2's weights w2 [C][9C] (K order as conv3x3s2) and bias b2;
 // conv1's output is never stored.
 constexpr int kStemFusedMaxC = 512;
+// tile_counter: an int that is 0 when the kernel starts (512-channel tiles
+// hand out their tiles from it).
 hipError_t stem12(hipStream_t s, const float* logmel, const ChunkInfo* chunks, int n_chunks, const uint4* wfrag,
-                  const bf16* w2, const float* b2, int C, bf16* out);
+                  const bf16* w2, const float* b2, int C, bf16* out, int* tile_counter);
 // conv 3x3 stride 2 pad 1 as an implicit GEMM over NHWC input [n_chunks][Hin][Win][C];
 // weights [C_out][9*C]
 // with k = (ci/32)*288 + (a*3+b)*32 + ci%32.  Output is NHWC
