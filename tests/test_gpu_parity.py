@@ -320,7 +320,8 @@ def test_bf16_fused_stem_widths(channels):
     partly filled 256-channel tile (64); a second output-channel tile holding
     one 32-channel group, whose other waves see only padding rows (288); the
     widest stem it takes, two full tiles and 16 slabs (512).  Clip lengths
-    give tail chunks and tiles at both ends of a chunk's 25 time columns."""
+    give tail chunks and tiles at both ends of a chunk's 25 time columns.
+    (C > 256 takes one 512-channel tile per pixel tile.)"""
     import dataclasses
     dims = dataclasses.replace(synth.DIMS_TINY, conv_channels=channels, dtype="bf16")
     w = synth.make_weights(dims, 140 + channels)
@@ -331,6 +332,26 @@ def test_bf16_fused_stem_widths(channels):
     out, taps = run_gpu(enc, clips, taps=True)
     rep = compare(dims, w, clips, out, taps)
     _print("fused stem width", rep)
+    enc.free()
+
+
+@pytest.mark.parametrize("channels", [288, 512])
+def test_bf16_fused_stem_many_tiles_per_workgroup(channels):
+    """The 512-channel fused stem over more pixel tiles than the GPU has CUs
+    (83 chunks, 415 tiles): its workgroups walk several tiles, taking them
+    from the tile counter, and set up each next tile inside the current one
+    (B operands and first patch in the last slab, the log-mel window two tiles
+    ahead), across clip boundaries and tail chunks."""
+    import dataclasses
+    dims = dataclasses.replace(synth.DIMS_TINY, conv_channels=channels, dtype="bf16")
+    w = synth.make_weights(dims, 150 + channels)
+    enc = make_encoder(dims, w)
+    lens = [16000 * 47 + 160 * 29 + 3, 16000 * 30, 16000 * 4 + 160 * 51]
+    clips = [synth.speech_like_clip(n, [97, i]) for i, n in enumerate(lens)]
+    _print(f"case: tiny bf16, {channels} stem channels, many tiles", lens)
+    out, taps = run_gpu(enc, clips, taps=True)
+    rep = compare(dims, w, clips, out, taps)
+    _print("fused stem many tiles", rep)
     enc.free()
 
 
