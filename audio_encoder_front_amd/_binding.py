@@ -275,7 +275,7 @@ def qa_encoder_set_profiling(enc: Encoder, enable: bool) -> None:
 
 
 def qa_encoder_set_max_lanes(enc: Encoder, n: int) -> None:
-    """Streams an encode may run on: 1 (the handle's alone) or 2 (the default)."""
+    """The most streams an encode may run on: 1 (the handle's alone) to 4 (the default)."""
     _check(_lib.qa_encoder_set_max_lanes(enc.handle, int(n)))
 
 

@@ -56,6 +56,12 @@ constexpr int64_t kMaxSamples = 20LL * 60 * 16000;   // a request hears up to 20
 constexpr int64_t kMaxFullInput = 30LL * 16000;      // bounded input of full-input attention (30 s)
 constexpr int kHop = 160;
 constexpr int kSplitKMaxTokens = 4096;   // residual GEMMs of smaller batches take split-K
+constexpr int kMaxLanes = 4;             // streams a large batch's layers may run on
+// lanes a batch past the split-K sizes runs as (at most the handle's
+// maximum): 3 up to kMidLaneTokens tokens, whose GEMMs fill few rounds of
+// CUs per lane, else 2 (measured: 4 lanes never paid; 3 against 2 was
+// 5.38 / 5.51 ms at 5,986 tokens, 15.80 / 15.54 ms at 15,600)
+constexpr int kMidLaneTokens = 8192;
 constexpr int kNfft = 400;
 constexpr int kBins = kNfft / 2 + 1;
 
@@ -228,10 +234,10 @@ struct qa_encoder {
     int esize = 4;                      // bytes per operand element (4 fp32, 2 bf16)
     hipStream_t stream = nullptr;
     int device = 0;
-    // second lane of the layers (see run_encode): a stream and the fork/join events
-    int max_lanes = 2;
-    hipStream_t lane = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    // further lanes of the layers (see run_encode): their streams and the fork/join events
+    int max_lanes = kMaxLanes;
+    hipStream_t lane[kMaxLanes - 1] = {};
+    hipEvent_t ev_fork = nullptr, ev_join[kMaxLanes - 1] = {};
     // weights + constants in one device allocation
     char* wbuf = nullptr;
     size_t conv1_frag = 0;              // bf16 MFMA fragments of conv1 (0: VALU kernel)
@@ -499,9 +505,11 @@ QA_API qa_encoder* qa_encoder_create(const qa_weights* w, const qa_dims* d) {
     if (st == hipSuccess) st = hipMalloc(&e->wbuf, pk.host.size());
     if (st == hipSuccess) st = hipMemcpy(e->wbuf, pk.host.data(), pk.host.size(), hipMemcpyHostToDevice);
     if (st == hipSuccess) st = hipHostMalloc(&e->flag_host, sizeof(int), hipHostMallocDefault);
-    if (st == hipSuccess) st = hipStreamCreateWithFlags(&e->lane, hipStreamNonBlocking);
+    for (int g = 0; g + 1 < kMaxLanes && st == hipSuccess; ++g) {
+        st = hipStreamCreateWithFlags(&e->lane[g], hipStreamNonBlocking);
+        if (st == hipSuccess) st = hipEventCreateWithFlags(&e->ev_join[g], hipEventDisableTiming);
+    }
     if (st == hipSuccess) st = hipEventCreateWithFlags(&e->ev_fork, hipEventDisableTiming);
-    if (st == hipSuccess) st = hipEventCreateWithFlags(&e->ev_join, hipEventDisableTiming);
     if (st != hipSuccess) {
         set_err("loading weights to the device failed: %s", hipGetErrorString(st));
         qa_encoder_free(e);
@@ -531,7 +539,7 @@ QA_API int qa_encoder_set_profiling(qa_encoder* e, int enable) {
 
 QA_API int qa_encoder_set_max_lanes(qa_encoder* e, int n) {
     if (!e) { set_err("encoder is NULL"); return QA_STATUS_INVALID_PARAMS; }
-    if (n != 1 && n != 2) { set_err("max lanes must be 1 or 2, got %d", n); return QA_STATUS_INVALID_PARAMS; }
+    if (n < 1 || n > kMaxLanes) { set_err("max lanes must be 1 .. %d, got %d", kMaxLanes, n); return QA_STATUS_INVALID_PARAMS; }
     e->max_lanes = n;
     return QA_STATUS_OK;
 }
@@ -589,9 +597,11 @@ QA_API void qa_encoder_free(qa_encoder* e) {
     if (e->pinned) (void)hipHostFree(e->pinned);
     if (e->flag_host) (void)hipHostFree(e->flag_host);
     for (hipEvent_t ev : e->ev_pool) (void)hipEventDestroy(ev);
-    if (e->lane) (void)hipStreamDestroy(e->lane);
+    for (int g = 0; g + 1 < kMaxLanes; ++g) {
+        if (e->lane[g]) (void)hipStreamDestroy(e->lane[g]);
+        if (e->ev_join[g]) (void)hipEventDestroy(e->ev_join[g]);
+    }
     if (e->ev_fork) (void)hipEventDestroy(e->ev_fork);
-    if (e->ev_join) (void)hipEventDestroy(e->ev_join);
     delete e;
 }
 
@@ -804,12 +814,12 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     } else {
         QA_LAUNCH("conv1", qa::conv1<T>(s, logmel, d_chunks, n_chunks, e->W<float>(e->conv1_w), e->W<float>(e->conv1_b), C, c1));
     }
-    // From there on a large batch runs as two lanes: the tokens split at the
-    // attention window whose start is nearest the middle (a chunk boundary),
-    // and each half runs the rest of its stem chunks, conv_out, the layers and
-    // the projection on a stream of its own (the caller's and the encoder's
-    // second stream).  One half's tiles then fill the CUs that the other
-    // half's last round of tiles leaves idle.  Rows (chunks, tokens) are
+    // From there on a large batch runs as two or three lanes: the tokens
+    // split at the attention windows whose starts are nearest the even split
+    // points (chunk boundaries), and each part runs the rest of its stem
+    // chunks, conv_out, the layers and the projection on a stream of its own
+    // (the caller's, then the encoder's own streams).  One part's tiles then
+    // fill the CUs that another part's last round of tiles leaves idle.  Rows (chunks, tokens) are
     // independent in every kernel and no window crosses the split, so the
     // outputs are bit-identical to one lane's.  Not with taps or with
     // profiling of every launch (one lane: each kernel's time is its own; with
@@ -817,34 +827,45 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
     // is timed on that lane's stream), nor for the small batches that take
     // split-K (one workspace for the partial sums).
     const bool every_launch = profiling && e->prof_only.empty();
-    const int lanes = (e->max_lanes == 2 && !taps && !every_launch && n_tok > kSplitKMaxTokens && n_win >= 2) ? 2 : 1;
+    const int lanes = (e->max_lanes > 1 && !taps && !every_launch && n_tok > kSplitKMaxTokens)
+                          ? std::min({e->max_lanes, n_win, n_tok <= kMidLaneTokens ? 3 : 2}) : 1;
     // If a launch fails after the fork, the call returns early: wait for what
-    // the second stream already holds, so that no work of this call outlives it
+    // the other streams already hold, so that no work of this call outlives it
     // (the next call may grow, and so free, the workspace).
     struct LaneGuard {
-        hipStream_t lane = nullptr;
+        hipStream_t lane[kMaxLanes - 1] = {};
         ~LaneGuard() {
-            if (lane) (void)hipStreamSynchronize(lane);
+            for (hipStream_t l : lane)
+                if (l) (void)hipStreamSynchronize(l);
         }
     } lane_guard;
-    int wsplit = n_win;
-    if (lanes == 2) {
-        lane_guard.lane = e->lane;
-        wsplit = 1;
-        for (int w = 2; w < n_win; ++w)
-            if (std::abs(2 * (int64_t)cu[w] - n_tok) < std::abs(2 * (int64_t)cu[wsplit] - n_tok)) wsplit = w;
-        QA_LAUNCH("fork", hipEventRecord(e->ev_fork, s));
-        QA_LAUNCH("fork", hipStreamWaitEvent(e->lane, e->ev_fork, 0));
+    // lane g takes windows [gw[g], gw[g + 1]): the split points are the window
+    // starts nearest g n_tok / lanes (distinct, increasing)
+    int gw[kMaxLanes + 1] = {0};
+    gw[lanes] = n_win;
+    for (int g = 1; g < lanes; ++g) {
+        int best = gw[g - 1] + 1;
+        for (int w = best + 1; w <= n_win - (lanes - g); ++w)
+            if (std::abs((int64_t)lanes * cu[w] - (int64_t)g * n_tok) < std::abs((int64_t)lanes * cu[best] - (int64_t)g * n_tok))
+                best = w;
+        gw[g] = best;
     }
-    const int gw[3] = {0, wsplit, n_win};
-    const hipStream_t gs[2] = {s, e->lane};
-    float* gpart = lanes == 2 ? nullptr : part;
-    const size_t gpe = lanes == 2 ? 0 : part_elems;
+    hipStream_t gs[kMaxLanes] = {s};
+    if (lanes > 1) {
+        QA_LAUNCH("fork", hipEventRecord(e->ev_fork, s));
+        for (int g = 1; g < lanes; ++g) {
+            lane_guard.lane[g - 1] = e->lane[g - 1];
+            gs[g] = e->lane[g - 1];
+            QA_LAUNCH("fork", hipStreamWaitEvent(gs[g], e->ev_fork, 0));
+        }
+    }
+    float* gpart = lanes > 1 ? nullptr : part;
+    const size_t gpe = lanes > 1 ? 0 : part_elems;
     const int UF = std::max(F, D);
     // The LayerNorm after a residual GEMM (conv_out, O-proj, FC2) runs inside
     // that GEMM's split-K reduction when it splits K (small batches); ln_ready
     // says that lane's h already holds the next LayerNorm's output.
-    bool ln_ready[2] = {false, false};
+    bool ln_ready[kMaxLanes] = {};
     auto ln_of = [&](int l, bool second) -> std::pair<const float*, const float*> {
         if (l >= d.n_layers) return {e->W<float>(e->post_ln_w), e->W<float>(e->post_ln_b)};
         const LayerW& lw = e->layers[l];
@@ -916,10 +937,10 @@ int run_encode(qa_encoder* e, const float* pcm, const int64_t* lengths, int n_cl
                 QA_LAUNCH("tap_layer0", hipMemcpyAsync(tl0, x, (size_t)n_tok * D * 4, hipMemcpyDeviceToDevice, s));
         }
     }
-    if (lanes == 2) {
-        QA_LAUNCH("join", hipEventRecord(e->ev_join, e->lane));
-        QA_LAUNCH("join", hipStreamWaitEvent(s, e->ev_join, 0));
-        lane_guard.lane = nullptr;   // the caller's stream now waits for the second one
+    for (int g = 1; g < lanes; ++g) {
+        QA_LAUNCH("join", hipEventRecord(e->ev_join[g - 1], gs[g]));
+        QA_LAUNCH("join", hipStreamWaitEvent(s, e->ev_join[g - 1], 0));
+        lane_guard.lane[g - 1] = nullptr;   // the caller's stream now waits for this one
     }
     QA_LAUNCH("flag", hipMemcpyAsync(e->flag_host, flag, sizeof(int), hipMemcpyDeviceToHost, s));
 #undef QA_LAUNCH

@@ -401,9 +401,10 @@ def main():
                     help="also time the layer GEMMs and conv2 through torch's vendor libraries (context)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for rocprofv3 byte counters)")
-    ap.add_argument("--lanes", type=int, default=2, choices=(1, 2),
-                    help="streams the timed workload may run on (qa_encoder_set_max_lanes; 1 for per-kernel "
-                         "profiles whose dispatches all cover the whole batch)")
+    ap.add_argument("--lanes", type=int, default=4, choices=(1, 2, 3, 4),
+                    help="the most streams the timed workload may run on (qa_encoder_set_max_lanes; the library "
+                         "picks 2 or 3 lanes by batch size; 1 for per-kernel profiles whose dispatches all cover "
+                         "the whole batch)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the encoder runs on a single MI355X and the library has no "

@@ -131,19 +131,20 @@ int64_t qa_encode_num_tokens(int64_t n_samples);
 qa_encoder *qa_encoder_create(const qa_weights *w, const qa_dims *d);
 
 /* Enqueue all later work of this handle on `hip_stream` (a hipStream_t;
- * NULL = the null stream).  A batch of more than 4,096 tokens also runs half
- * of its layers on a second stream the handle owns (created with it, default
- * priority), forked from and joined back into `hip_stream` by events inside
- * the call, so that later work on `hip_stream` sees every result.  Returns
- * QA_STATUS_OK or INVALID_PARAMS. */
+ * NULL = the null stream).  A batch of more than 4,096 tokens also runs part
+ * of its layers on one or two more streams the handle owns (created with it,
+ * default priority), forked from and joined back into `hip_stream` by events
+ * inside the call, so that later work on `hip_stream` sees every result.
+ * Returns QA_STATUS_OK or INVALID_PARAMS. */
 int qa_encoder_set_stream(qa_encoder *e, void *hip_stream);
 
-/* Streams a qa_encode call may run on: 1 keeps every launch on the handle's
- * stream; 2 (the default) lets a batch of more than 4,096 tokens run half of
- * its tokens, from conv3 on, on the handle's second stream (see
- * qa_encoder_set_stream).  The results are bit-identical either way (rows are
- * independent in every kernel and the split falls between attention windows).
- * Returns QA_STATUS_OK, or INVALID_PARAMS for a NULL handle or n not 1 or 2. */
+/* The most streams a qa_encode call may run on, 1 to 4 (default 4): a batch
+ * of more than 4,096 tokens runs, from conv3 on, as 3 parts (up to 8,192
+ * tokens) or 2 parts (more), each on a stream of its own (see
+ * qa_encoder_set_stream), capped at n; 1 keeps every launch on the handle's
+ * stream.  The results are bit-identical either way (rows are independent in
+ * every kernel and the splits fall between attention windows).  Returns
+ * QA_STATUS_OK, or INVALID_PARAMS for a NULL handle or n outside 1 .. 4. */
 int qa_encoder_set_max_lanes(qa_encoder *e, int n);
 
 /* Encode a packed batch: every step of the tower above, one packed forward

@@ -36,21 +36,21 @@ def test_tiny_full_input_ragged_batch(tiny_full):
     print("tiny full-input", rep, flush=True)
 
 
-def test_tiny_full_input_two_lanes(tiny_full):
+def test_tiny_full_input_lanes(tiny_full):
     """4,316 tokens (past the split-K sizes): without taps the stem, the layers
-    and the head run as two lanes split at a clip boundary, each lane's
+    and the head run as three lanes split at clip boundaries, each lane's
     segments through the long-segment kernel; bit-identical to the one-lane
     run with taps, which matches the oracle on every clip."""
     dims, w, enc = tiny_full
     lens = [480000] * 10 + [16000 * 25 + 77, 16000 * 7]
     clips = [synth.speech_like_clip(n, [92, i]) for i, n in enumerate(lens)]
-    print("case: tiny encoder, full-input attention, two lanes", flush=True)
+    print("case: tiny encoder, full-input attention, lanes", flush=True)
     out2, _ = run_gpu(enc, clips)
     out, taps = run_gpu(enc, clips, taps=True)
     assert out.shape[0] == 4316
     assert np.array_equal(out2, out)
     rep = compare(dims, w, clips, out, taps)
-    print("tiny full-input two lanes", rep, flush=True)
+    print("tiny full-input lanes", rep, flush=True)
 
 
 def test_full_input_rejects_clips_over_30s(tiny_full):

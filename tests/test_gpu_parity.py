@@ -175,16 +175,17 @@ def test_b06_packed_32_clips(b06):
     clips = synth.make_audio(wl32)
     _print("case: 0.6B bf16, 32 clips U(1,30) s")
     out, taps = run_gpu(enc, clips, taps=True)
-    # without taps the batch (5,986 tokens) runs as two lanes: bit-identical;
-    # and pinned to one stream (max lanes 1) without taps
+    # without taps the batch (5,986 tokens) runs as three lanes by default,
+    # as two with at most 2 streams, as one with 1: all bit-identical
     import audio_encoder_front_amd as qa
-    out2, _ = run_gpu(enc, clips)
-    assert np.array_equal(out2, out)
-    qa.qa_encoder_set_max_lanes(enc, 1)
-    out1, _ = run_gpu(enc, clips)
-    qa.qa_encoder_set_max_lanes(enc, 2)
-    assert np.array_equal(out1, out)
-    for bad in (0, 3):
+    out3, _ = run_gpu(enc, clips)
+    assert np.array_equal(out3, out)
+    for n in (2, 1):
+        qa.qa_encoder_set_max_lanes(enc, n)
+        outn, _ = run_gpu(enc, clips)
+        assert np.array_equal(outn, out), f"max lanes {n}"
+    qa.qa_encoder_set_max_lanes(enc, 4)
+    for bad in (0, 5):
         with pytest.raises(qa.QAError):
             qa.qa_encoder_set_max_lanes(enc, bad)
     # the bench's timed steps: events around the fused stem only, lanes kept
@@ -259,23 +260,31 @@ def test_b17_packed_16_clips_every_window(b17):
     assert len(rows) >= 8
 
 
-def test_two_lanes_fp32(tiny):
+def test_lanes_fp32(tiny):
     """Batches past the split-K sizes run conv_out, the layers and the
-    projection as two lanes on two streams, split at the window whose start
-    is nearest the middle (here token 2,184 of 4,292, inside the 300 s clip);
-    with taps on they run as one.  The two runs are bit-identical, and the
-    windows at the split, the ends and the second clip match the oracle."""
+    projection as parts on separate streams, split at the windows whose
+    starts are nearest the even split points: three parts for this batch of
+    4,292 tokens (at tokens 1,456 and 2,912, inside the 300 s clip), two
+    when the handle allows at most 2 streams (token 2,184); with taps on
+    they run as one.  All runs are bit-identical, and the windows at the
+    splits, the ends and the second clip match the oracle."""
+    import audio_encoder_front_amd as qa
     wl, _, w, enc = tiny
     lens = [16000 * 300, 16000 * 30 + 160 * 13 + 3]
     clips = [synth.speech_like_clip(n, [97, i]) for i, n in enumerate(lens)]
-    _print("case: tiny fp32, two lanes", lens)
+    _print("case: tiny fp32, lanes", lens)
+    out3, _ = run_gpu(enc, clips)
+    qa.qa_encoder_set_max_lanes(enc, 2)
     out2, _ = run_gpu(enc, clips)
+    qa.qa_encoder_set_max_lanes(enc, 4)
     out, taps = run_gpu(enc, clips, taps=True)
     assert out.shape[0] == 4292
+    assert np.array_equal(out3, out)
     assert np.array_equal(out2, out)
     rep = compare(wl.dims, w, clips, out, taps,
-                  windows_per_clip=lambda ci, nw: [0, 19, 20, 21, 22, nw - 1] if ci == 0 else range(nw))
-    _print("two lanes", rep)
+                  windows_per_clip=lambda ci, nw: [0, 12, 13, 14, 19, 20, 21, 22, 26, 27, 28, nw - 1]
+                  if ci == 0 else range(nw))
+    _print("lanes", rep)
 
 
 @pytest.mark.parametrize("base,window_chunks", [("tiny", 9), ("tiny", 1), ("b06", 9), ("b06", 1)])

@@ -32,7 +32,7 @@ def _pair(enc, clips):
 @pytest.mark.parametrize("name,big,small", [
     ("tiny", [32000, 150000, 201], [16160]),
     ("b06_1", [480000], [16000 * 7 + 160 * 37 + 11, 0, 40000]),
-    # 4,292 tokens: past the split-K sizes, so the layers run as two lanes
+    # 4,292 tokens: past the split-K sizes, so the layers run as three lanes
     ("tiny_bf16", [16000 * 300, 16000 * 30 + 160 * 13 + 3], [16000 * 100 + 7]),
 ])
 def test_noalloc_matches_qa_encode(name, big, small):
