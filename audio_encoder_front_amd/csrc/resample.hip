@@ -10,6 +10,10 @@
 //   * output n is the filtered zero-stuffed input at upsampled index n down
 //     (zero delay), with zeros outside the clip; n_out = ceil(n_in up / down).
 //
+// Two kernels compute it: resample_phase_kernel (tables of at most 64 taps per
+// phase and 1,024 phases, i.e. the common rates: each thread keeps one
+// phase's row in registers, see there) and resample_kernel (any table).
+//
 // Polyphase form: of the 2 half + 1 taps only those landing on original
 // samples contribute, i.e. taps p + j up with p = (n down + half) mod up, so
 // output n is a dot product of one table row hp[p][0..L) (L = ceil(taps / up),
@@ -44,6 +48,7 @@ constexpr int kResampleHalfFactor = 10;
 constexpr int kResampleThreads = 256;
 constexpr int kResampleMaxWindow = 16384;      // staged input samples per workgroup (64 KB of LDS)
 constexpr int kResampleMaxLdsTable = 12288;    // tables up to 48 KB (padded rows) are staged in LDS too
+constexpr int kResamplePhaseWindow = 8192;     // the phase-major kernel's window target (32 KB of LDS)
 
 // LDS row stride of the table: L (a multiple of 4) rounded up to 4 x an odd number.
 __host__ __device__ constexpr int resample_lds_row(int L) { return (L / 4) % 2 ? L : L + 4; }
@@ -113,6 +118,72 @@ __global__ __launch_bounds__(kResampleThreads) void resample_kernel(const float*
                 a1 = fmaf(h.y, win[b - 1], a1);
                 a2 = fmaf(h.z, win[b - 2], a2);
                 a3 = fmaf(h.w, win[b - 3], a3);
+            }
+            y[n] = (a0 + a1) + (a2 + a3);
+        }
+    }
+}
+
+// Tables of up to 64 taps per phase and up to 1,024 phases (every rate the
+// front end meets in practice: 44.1, 48, 22.05, 11.025, 8 kHz ...): outputs
+// n and n + up use the same table row, so each thread takes the outputs of
+// one phase and holds that row in registers for the whole kernel, and only
+// the input window is read from LDS (half the LDS traffic of
+// resample_kernel, whose table reads cost as much LDS time as its window
+// reads).  A workgroup of T = up C threads (C = ceil(256 / up) columns)
+// covers blocks of M = T rows consecutive outputs (M a multiple of up, so
+// thread (i, c) = (tid % up, tid / up) always has phase (i down + half) mod
+// up) and stages each block's input window in LDS; the dot products and
+// their summation order are resample_kernel's, so the outputs are the same.
+template <int LQ>
+__global__ __launch_bounds__(1024) void resample_phase_kernel(const float* __restrict__ x, int64_t n_in,
+                                                              float* __restrict__ y, int64_t n_out,
+                                                              const float* __restrict__ hp, int up, int down,
+                                                              int half, int C, int rows, int64_t n_blocks) {
+    extern __shared__ float win[];
+    constexpr int L = 4 * LQ;
+    const int T = (int)blockDim.x, tid = (int)threadIdx.x;
+    const int i = tid % up, c = tid / up;
+    const int64_t M = (int64_t)T * rows;
+    const int p = (int)(((int64_t)i * down + half) % up);
+    float4 h[LQ];
+    const float4* hr = reinterpret_cast<const float4*>(hp + (size_t)p * L);
+#pragma unroll
+    for (int j4 = 0; j4 < LQ; ++j4) h[j4] = hr[j4];
+    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+        const int64_t n0 = blk * M;
+        const int64_t n_last = (n0 + M < n_out ? n0 + M : n_out) - 1;
+        const int64_t lo = (n0 * down + half) / up - (L - 1);           // lowest input sample read
+        const int cnt = (int)((n_last * down + half) / up - lo + 1);   // <= the staged window (host-checked)
+        __syncthreads();                                                // previous window consumed
+        for (int i0 = 0; i0 < cnt; i0 += 8 * T) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = i0 + u * T + tid;
+                const int64_t g = lo + k;
+                v[u] = k < cnt && g >= 0 && g < n_in ? x[g] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = i0 + u * T + tid;
+                if (k < cnt) win[k] = v[u];
+            }
+        }
+        __syncthreads();
+        for (int r = 0; r < rows; ++r) {
+            const int64_t n = n0 + ((int64_t)r * C + c) * up + i;
+            if (n > n_last) break;
+            const int64_t t = n * down + half;           // upsampled index met by tap 0
+            const int qs = (int)(t / up - lo);           // staged index of input sample q = t / up
+            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+            for (int j4 = 0; j4 < LQ; ++j4) {            // tap p + j up meets sample q - j
+                const int b = qs - 4 * j4;
+                a0 = fmaf(h[j4].x, win[b], a0);
+                a1 = fmaf(h[j4].y, win[b - 1], a1);
+                a2 = fmaf(h[j4].z, win[b - 2], a2);
+                a3 = fmaf(h[j4].w, win[b - 3], a3);
             }
             y[n] = (a0 + a1) + (a2 + a3);
         }
@@ -201,6 +272,37 @@ QA_API int qa_resample(qa_resampler* r, void* hip_stream, const float* in, int64
     }
     const int64_t n_out = qa_resample_length(n_in, r->rate);
     if (n_out == 0) return QA_STATUS_OK;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (r->L <= 64 && r->up <= 1024) {
+        // phase-major kernel: T = up C threads, blocks of T rows outputs whose
+        // window stays within kResamplePhaseWindow samples
+        const int C = r->up >= 256 ? 1 : (256 + r->up - 1) / r->up, T = r->up * C;
+        auto window = [&](int64_t m) { return (m - 1) * r->down / r->up + 2 + r->L; };
+        int rows = 8;
+        while (rows > 1 && window((int64_t)T * rows) > qa::kResamplePhaseWindow) --rows;
+        if (window((int64_t)T * rows) <= qa::kResampleMaxWindow) {
+            const int64_t M = (int64_t)T * rows, blocks = (n_out + M - 1) / M;
+            const size_t lds = (size_t)window(M) * sizeof(float);
+            const int per_cu = std::max(1, std::min({8, (int)(160 * 1024 / lds), 2048 / T}));
+            const unsigned grid = (unsigned)std::min<int64_t>(blocks, (int64_t)cus * per_cu);
+            switch (r->L / 4) {
+#define QA_RSP(q) case q: qa::resample_phase_kernel<q><<<grid, T, lds, s>>>(in, n_in, out, n_out, r->table, r->up, \
+                                                                        r->down, r->half, C, rows, blocks); break;
+                QA_RSP(1) QA_RSP(2) QA_RSP(3) QA_RSP(4) QA_RSP(5) QA_RSP(6) QA_RSP(7) QA_RSP(8)
+                QA_RSP(9) QA_RSP(10) QA_RSP(11) QA_RSP(12) QA_RSP(13) QA_RSP(14) QA_RSP(15) QA_RSP(16)
+#undef QA_RSP
+                default: break;
+            }
+            const hipError_t st = hipGetLastError();
+            if (st != hipSuccess) {
+                qa::set_error_message(hipGetErrorString(st));
+                return QA_STATUS_ENCODE_FAILED;
+            }
+            return QA_STATUS_OK;
+        }
+    }
     // outputs per thread: the largest of 4, 2, 1 whose input window fits the LDS stage
     auto window = [&](int opb) { return (int64_t)(opb - 1) * r->down / r->up + 2 + r->L; };
     int opt = 4;
@@ -216,11 +318,8 @@ QA_API int qa_resample(qa_resampler* r, void* hip_stream, const float* in, int64
     const size_t lds = ((size_t)window(qa::kResampleThreads * opt) + (tlds ? (size_t)lt : 0)) * sizeof(float);
     // persistent grid: a few workgroups per CU (as many as the LDS allows, at
     // most 4), each staging the table once
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int per_cu = std::max(1, std::min(4, (int)(160 * 1024 / std::max<size_t>(lds, 1))));
     const unsigned grid = (unsigned)std::min<int64_t>(blocks, (int64_t)cus * per_cu);
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
 #define QA_RS(o, t) qa::resample_kernel<o, t><<<grid, qa::kResampleThreads, lds, s>>>( \
         in, n_in, out, n_out, r->table, r->up, r->down, r->half, r->L, blocks)
     if (tlds) {
