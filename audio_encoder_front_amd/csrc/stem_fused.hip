@@ -391,6 +391,12 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
                     __builtin_amdgcn_sched_barrier(0);
                 };
                 if (work && wave < 4) conv1_phase();
+                // The MFMA section runs at wave priority 1: when both waves of
+                // the SIMD can issue, the matrix instruction goes first and the
+                // sibling's VALU phase takes the cycles in between.
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(1);
+                __builtin_amdgcn_sched_barrier(0);
                 uint4 ring[kFsStream];
 #pragma unroll
                 for (int q = 0; q < kFsStream; ++q) ring[q] = read_frag(q / 10, q % 10);
@@ -410,6 +416,9 @@ __global__ __launch_bounds__(512) void stem12_kernel(const float* __restrict__ l
                         __builtin_amdgcn_sched_barrier(0);   // keeps the register ring from being hoisted
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
                 if (work && wave >= 4) conv1_phase();
             }
             if (wa_next) __builtin_amdgcn_s_waitcnt(0x0F70);   // the conv1 fragments two slabs ahead landed

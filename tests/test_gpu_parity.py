@@ -323,14 +323,14 @@ def test_bf16_wide_stem_valu_conv1():
     enc.free()
 
 
-@pytest.mark.parametrize("channels", [64, 288, 512])
+@pytest.mark.parametrize("channels", [64, 288, 416, 480, 512])
 def test_bf16_fused_stem_widths(channels):
     """The fused conv1-in-conv2 kernel at other stem widths: 2 slabs and one
-    partly filled 256-channel tile (64); a second output-channel tile holding
-    one 32-channel group, whose other waves see only padding rows (288); the
-    widest stem it takes, two full tiles and 16 slabs (512).  Clip lengths
-    give tail chunks and tiles at both ends of a chunk's 25 time columns.
-    (C > 256 takes one 512-channel tile per pixel tile.)"""
+    partly filled 256-channel tile (64); 512-channel tiles of which one
+    32-channel group (288), 416 channels, or 480 (the 0.6B / 1.7B stem) are
+    real and the other waves' rows padding; the widest stem it takes, every
+    row real and 16 slabs (512).  Clip lengths give tail chunks and tiles at
+    both ends of a chunk's 25 time columns."""
     import dataclasses
     dims = dataclasses.replace(synth.DIMS_TINY, conv_channels=channels, dtype="bf16")
     w = synth.make_weights(dims, 140 + channels)
@@ -344,7 +344,7 @@ def test_bf16_fused_stem_widths(channels):
     enc.free()
 
 
-@pytest.mark.parametrize("channels", [288, 512])
+@pytest.mark.parametrize("channels", [288, 480, 512])
 def test_bf16_fused_stem_many_tiles_per_workgroup(channels):
     """The 512-channel fused stem over more pixel tiles than the GPU has CUs
     (83 chunks, 415 tiles): its workgroups walk several tiles, taking them
